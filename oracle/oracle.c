@@ -1,0 +1,403 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the paged KV-cache hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark load it.  It shares no header, helper or constant with the
+ * HIP library: every layout rule below is written out here on its own.
+ *
+ * Three functions, each the plain definition from the pages:
+ *
+ *   orc_prepare    -- the flat-batch index tensors ("Building the Batch",
+ *                     sections "How they are computed" and "Reading and
+ *                     writing the KV cache"; "vLLM's Model Runner -- the
+ *                     Persistent Batch, in Source", "The two things this
+ *                     method returns").
+ *   orc_kv_write   -- each new token's K and V row copied to the cache slot
+ *                     named by slot_mapping ("Inside vLLM: Following One
+ *                     Request from the API to GPU Execution", Part 5, the
+ *                     write path through slot_mapping).
+ *   orc_attention  -- per request, gather the logical blocks named by the
+ *                     block table into contiguous K and V, then naive causal
+ *                     softmax attention in fp64 ("How vLLM Works Internally:
+ *                     A Deep Dive", "How the Kernel Works", its four steps;
+ *                     "Inside vLLM...", Part 5, the block_table read loop).
+ *
+ * Cache layout (an interface fact, not part of the method; the pages leave the
+ * layout open): K pool [num_blocks][num_kv_heads][block_size][head_dim],
+ * V pool [num_blocks][num_kv_heads][head_dim][block_size], row-major.
+ *
+ * Readings of points the pages leave open (each also listed in the design
+ * notes of the repository):
+ *   - causal alignment: the query at in-chunk offset t of a request with
+ *     q_len new tokens and seq_len total tokens sits at absolute position
+ *     p = seq_len - q_len + t (= num_computed_tokens + t) and sees keys
+ *     0..p inclusive;
+ *   - GQA: q head h reads kv head h / (num_q_heads / num_kv_heads);
+ *   - slot -1 in slot_mapping means "no write" (a padding row);
+ *   - the query_start_loc entries past num_reqs are filled with the token
+ *     total so the array stays non-decreasing.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG 1      /* null pointer or non-positive size            */
+#define ORC_ERR_RANGE 2    /* block id, logical block or slot out of range  */
+#define ORC_ERR_DUP 3      /* two tokens name the same cache slot           */
+#define ORC_ERR_PRECOND 4  /* q_len > seq_len, or a row outside the batch   */
+#define ORC_ERR_NOMEM 5
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* prepare                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For requests r = 0..R-1 in order (nst = num_scheduled_tokens,
+ * nct = num_computed_tokens):
+ *   qsl[0] = 0, qsl[r+1] = qsl[r] + nst[r]           (prefix sum of the chunk
+ *                                                      lengths)
+ *   seq_lens[r] = nct[r] + nst[r]                     (length once this step's
+ *                                                      tokens are in the cache)
+ *   logits_indices[r] = qsl[r+1] - 1                  (last row of the request)
+ *   for t in 0..nst[r]-1, row i = qsl[r] + t:
+ *     req_indices[i] = r
+ *     positions[i]   = nct[r] + t                     (computed tokens + offset
+ *                                                      inside the chunk)
+ *     slot[i] = block_table[r][positions[i] / bs] * bs + positions[i] % bs
+ *   qsl[R+1 .. qsl_len-1] = T                         (non-decreasing tail)
+ * Returns ORC_ERR_RANGE when a needed block-table column is >= bt_cols or a
+ * block id lies outside [0, num_blocks).  *num_tokens_out receives T.
+ */
+int orc_prepare(const int32_t* nst, const int32_t* nct, const int32_t* block_table,
+                int64_t bt_stride, int32_t bt_cols, int32_t num_reqs, int32_t qsl_len,
+                int32_t block_size, int64_t num_blocks, int32_t* req_indices,
+                int32_t* positions, int64_t* slot_mapping, int32_t* qsl, int32_t* seq_lens,
+                int32_t* logits_indices, int64_t* num_tokens_out) {
+  if (!nst || !nct || !qsl || !seq_lens || !logits_indices || num_reqs < 0 ||
+      qsl_len < num_reqs + 1 || block_size <= 0)
+    return ORC_ERR_ARG;
+  qsl[0] = 0;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    if (nst[r] < 0 || nct[r] < 0) return ORC_ERR_ARG;
+    qsl[r + 1] = qsl[r] + nst[r];
+    seq_lens[r] = nct[r] + nst[r];
+    logits_indices[r] = qsl[r + 1] - 1;
+  }
+  const int32_t total = qsl[num_reqs];
+  for (int32_t k = num_reqs + 1; k < qsl_len; ++k) qsl[k] = total;
+  if (num_tokens_out) *num_tokens_out = total;
+  if (total > 0 && (!req_indices || !positions || !slot_mapping)) return ORC_ERR_ARG;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    for (int32_t t = 0; t < nst[r]; ++t) {
+      const int32_t i = qsl[r] + t;
+      const int32_t pos = nct[r] + t;
+      req_indices[i] = r;
+      positions[i] = pos;
+      const int32_t logical = pos / block_size;
+      if (!block_table || logical >= bt_cols) return ORC_ERR_RANGE;
+      const int32_t phys = block_table[(int64_t)r * bt_stride + logical];
+      if (phys < 0 || phys >= num_blocks) return ORC_ERR_RANGE;
+      slot_mapping[i] = (int64_t)phys * block_size + pos % block_size;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* kv_write                                                                  */
+/* ------------------------------------------------------------------------ */
+
+static int64_t orc_k_elem(int64_t block, int32_t head, int32_t tok, int32_t dim,
+                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim) {
+  return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;
+}
+
+static int64_t orc_v_elem(int64_t block, int32_t head, int32_t tok, int32_t dim,
+                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim) {
+  return ((block * num_kv_heads + head) * (int64_t)head_dim + dim) * block_size + tok;
+}
+
+static int cmp_i64(const void* a, const void* b) {
+  const int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+  return (x > y) - (x < y);
+}
+
+/*
+ * For every token i with slot s = slot_mapping[i] >= 0 and every kv head h:
+ * K row key[i][h][:] goes to block s / bs, in-block offset s % bs, head h of
+ * the K pool; the V row likewise to the V pool.  The bytes are copied as they
+ * are (a write, no arithmetic).  key/value rows are [T][num_kv_heads][head_dim]
+ * with a row stride (elements between consecutive tokens) of key_row_stride /
+ * value_row_stride.  Rejects slots outside the pool and duplicate slots.
+ */
+int orc_kv_write(const void* key, const void* value, int64_t key_row_stride,
+                 int64_t value_row_stride, void* key_cache, void* value_cache,
+                 int64_t num_blocks, const int64_t* slot_mapping, int32_t num_tokens,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                 int32_t elem_bytes) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      (elem_bytes != 2 && elem_bytes != 4))
+    return ORC_ERR_ARG;
+  if (num_tokens == 0) return ORC_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return ORC_ERR_ARG;
+  const int64_t pool_slots = num_blocks * block_size;
+  int64_t* seen = (int64_t*)malloc(sizeof(int64_t) * (size_t)num_tokens);
+  if (!seen) return ORC_ERR_NOMEM;
+  int32_t n_seen = 0;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t s = slot_mapping[i];
+    if (s < 0) continue;
+    if (s >= pool_slots) { free(seen); return ORC_ERR_RANGE; }
+    seen[n_seen++] = s;
+  }
+  qsort(seen, (size_t)n_seen, sizeof(int64_t), cmp_i64);
+  for (int32_t k = 1; k < n_seen; ++k)
+    if (seen[k] == seen[k - 1]) { free(seen); return ORC_ERR_DUP; }
+  free(seen);
+
+  const char* ksrc = (const char*)key;
+  const char* vsrc = (const char*)value;
+  char* kdst = (char*)key_cache;
+  char* vdst = (char*)value_cache;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t s = slot_mapping[i];
+    if (s < 0) continue;
+    const int64_t block = s / block_size;
+    const int32_t off = (int32_t)(s % block_size);
+    for (int32_t h = 0; h < num_kv_heads; ++h) {
+      for (int32_t c = 0; c < head_dim; ++c) {
+        const int64_t src_k = (int64_t)i * key_row_stride + (int64_t)h * head_dim + c;
+        const int64_t src_v = (int64_t)i * value_row_stride + (int64_t)h * head_dim + c;
+        const int64_t dk = orc_k_elem(block, h, off, c, num_kv_heads, block_size, head_dim);
+        const int64_t dv = orc_v_elem(block, h, off, c, num_kv_heads, block_size, head_dim);
+        memcpy(kdst + dk * elem_bytes, ksrc + src_k * elem_bytes, (size_t)elem_bytes);
+        memcpy(vdst + dv * elem_bytes, vsrc + src_v * elem_bytes, (size_t)elem_bytes);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* attention                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Exact widening of one stored element to fp64.  bf16 is the top half of an
+ * IEEE binary32, so shifting its 16 bits up gives the same value as fp32. */
+static double orc_load(const void* base, int64_t idx, int32_t dtype) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+typedef struct {
+  int32_t req;      /* request index                              */
+  int32_t kv_head;  /* kv head                                    */
+  int32_t first;    /* first entry in the sorted selection        */
+  int32_t count;    /* number of selected rows in this work item  */
+} orc_item;
+
+typedef struct {
+  int32_t row;  /* flat row index                  */
+  int32_t sel;  /* position in the caller's list   */
+  int32_t req;  /* request owning the row          */
+} orc_sel;
+
+static int cmp_sel(const void* a, const void* b) {
+  const orc_sel* x = (const orc_sel*)a;
+  const orc_sel* y = (const orc_sel*)b;
+  if (x->req != y->req) return (x->req > y->req) - (x->req < y->req);
+  return (x->row > y->row) - (x->row < y->row);
+}
+
+/*
+ * out[k][h][:] for each selected flat row rows[k] (all T rows when rows is
+ * NULL, in which case num_rows must equal qsl[num_reqs]) and each q head h:
+ *
+ *   r   = the request with qsl[r] <= row < qsl[r+1]
+ *   L   = seq_lens[r], q_len = qsl[r+1] - qsl[r], t = row - qsl[r]
+ *   p   = L - q_len + t                                  (absolute position)
+ *   g   = h / (num_q_heads / num_kv_heads)
+ *   Kr, Vr = the request's first p+1 cache rows for head g, gathered in
+ *            logical order: token j comes from physical block
+ *            block_table[r][j / bs], in-block offset j % bs
+ *   s_j = scale * sum_c q[row][h][c] * Kr[j][c]          for j = 0..p
+ *   w_j = exp(s_j - max_j s_j)
+ *   out = sum_j w_j * Vr[j][:] / sum_j w_j
+ *
+ * Everything is fp64; inputs (fp32 or bf16) are widened exactly.  q rows are
+ * [T][num_q_heads][head_dim] with row stride q_row_stride elements.
+ * Returns ORC_ERR_PRECOND when q_len > seq_len for a request that has a
+ * selected row, ORC_ERR_RANGE when a needed table column or block id is out of
+ * range.  num_threads <= 0 uses the OpenMP default.
+ */
+int orc_attention(const void* q, int64_t q_row_stride, const void* key_cache,
+                  const void* value_cache, int32_t dtype, const int32_t* qsl,
+                  const int32_t* seq_lens, const int32_t* block_table, int64_t bt_stride,
+                  int32_t bt_cols, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int64_t num_blocks, double scale,
+                  const int32_t* rows, int32_t num_rows, double* out, int32_t num_threads) {
+  if (!q || !key_cache || !value_cache || !qsl || !seq_lens || !block_table || !out ||
+      num_reqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_rows < 0 || num_q_heads % num_kv_heads != 0 ||
+      (dtype != ORC_F32 && dtype != ORC_BF16))
+    return ORC_ERR_ARG;
+  const int32_t total_rows = qsl[num_reqs];
+  if (!rows && num_rows != total_rows) return ORC_ERR_ARG;
+  if (num_rows == 0) return ORC_OK;
+  const int32_t group = num_q_heads / num_kv_heads;
+
+  /* Tag every selected row with its request, then sort by (request, row). */
+  orc_sel* sel = (orc_sel*)malloc(sizeof(orc_sel) * (size_t)num_rows);
+  if (!sel) return ORC_ERR_NOMEM;
+  for (int32_t k = 0; k < num_rows; ++k) {
+    const int32_t row = rows ? rows[k] : k;
+    if (row < 0 || row >= total_rows) { free(sel); return ORC_ERR_PRECOND; }
+    int32_t lo = 0, hi = num_reqs - 1; /* last r with qsl[r] <= row */
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) / 2;
+      if (qsl[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    while (lo < num_reqs - 1 && qsl[lo + 1] <= row) ++lo;
+    sel[k].row = row;
+    sel[k].sel = k;
+    sel[k].req = lo;
+  }
+  qsort(sel, (size_t)num_rows, sizeof(orc_sel), cmp_sel);
+
+  /* Check the preconditions and cut the selection into work items:
+   * (request, kv head, up to 16 consecutive selected rows). */
+  const int32_t chunk = 16;
+  int32_t n_items = 0;
+  for (int32_t k = 0; k < num_rows;) {
+    const int32_t r = sel[k].req;
+    const int32_t q_len = qsl[r + 1] - qsl[r];
+    const int32_t L = seq_lens[r];
+    if (q_len > L) { free(sel); return ORC_ERR_PRECOND; }
+    int32_t e = k;
+    while (e < num_rows && sel[e].req == r) ++e;
+    int32_t max_pos = L - q_len + (sel[e - 1].row - qsl[r]);
+    const int32_t needed_blocks = max_pos / block_size + 1;
+    if (needed_blocks > bt_cols) { free(sel); return ORC_ERR_RANGE; }
+    for (int32_t j = 0; j < needed_blocks; ++j) {
+      const int32_t b = block_table[(int64_t)r * bt_stride + j];
+      if (b < 0 || b >= num_blocks) { free(sel); return ORC_ERR_RANGE; }
+    }
+    n_items += num_kv_heads * ((e - k + chunk - 1) / chunk);
+    k = e;
+  }
+  orc_item* items = (orc_item*)malloc(sizeof(orc_item) * (size_t)n_items);
+  if (!items) { free(sel); return ORC_ERR_NOMEM; }
+  int32_t it = 0;
+  for (int32_t k = 0; k < num_rows;) {
+    const int32_t r = sel[k].req;
+    int32_t e = k;
+    while (e < num_rows && sel[e].req == r) ++e;
+    for (int32_t g = 0; g < num_kv_heads; ++g)
+      for (int32_t c = k; c < e; c += chunk) {
+        items[it].req = r;
+        items[it].kv_head = g;
+        items[it].first = c;
+        items[it].count = (e - c < chunk) ? (e - c) : chunk;
+        ++it;
+      }
+    k = e;
+  }
+
+  int status = ORC_OK;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+  (void)num_threads;
+#endif
+#pragma omp parallel
+  {
+    double* Kr = NULL;
+    double* Vr = NULL;
+    double* s = NULL;
+    int64_t cap = 0;
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t w = 0; w < n_items; ++w) {
+      const orc_item item = items[w];
+      const int32_t r = item.req, g = item.kv_head;
+      const int32_t q_len = qsl[r + 1] - qsl[r];
+      const int32_t L = seq_lens[r];
+      const orc_sel* last = &sel[item.first + item.count - 1];
+      const int32_t n_keys = L - q_len + (last->row - qsl[r]) + 1;
+      if (n_keys > cap) {
+        free(Kr); free(Vr); free(s);
+        cap = n_keys;
+        Kr = (double*)malloc(sizeof(double) * (size_t)cap * head_dim);
+        Vr = (double*)malloc(sizeof(double) * (size_t)cap * head_dim);
+        s = (double*)malloc(sizeof(double) * (size_t)cap);
+        if (!Kr || !Vr || !s) {
+#pragma omp atomic write
+          status = ORC_ERR_NOMEM;
+          cap = 0;
+          continue;
+        }
+      }
+      /* Gather: logical token j lives in block_table[r][j / bs] at j % bs. */
+      for (int32_t j = 0; j < n_keys; ++j) {
+        const int64_t phys = block_table[(int64_t)r * bt_stride + j / block_size];
+        const int32_t off = j % block_size;
+        for (int32_t c = 0; c < head_dim; ++c) {
+          Kr[(int64_t)j * head_dim + c] = orc_load(
+              key_cache, orc_k_elem(phys, g, off, c, num_kv_heads, block_size, head_dim), dtype);
+          Vr[(int64_t)j * head_dim + c] = orc_load(
+              value_cache, orc_v_elem(phys, g, off, c, num_kv_heads, block_size, head_dim), dtype);
+        }
+      }
+      for (int32_t k = item.first; k < item.first + item.count; ++k) {
+        const int32_t row = sel[k].row;
+        const int32_t p = L - q_len + (row - qsl[r]);
+        for (int32_t h = g * group; h < (g + 1) * group; ++h) {
+          double* o = out + ((int64_t)sel[k].sel * num_q_heads + h) * head_dim;
+          const int64_t qbase = (int64_t)row * q_row_stride + (int64_t)h * head_dim;
+          double m = -INFINITY;
+          for (int32_t j = 0; j <= p; ++j) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < head_dim; ++c)
+              acc += orc_load(q, qbase + c, dtype) * Kr[(int64_t)j * head_dim + c];
+            s[j] = scale * acc;
+            if (s[j] > m) m = s[j];
+          }
+          double denom = 0.0;
+          for (int32_t j = 0; j <= p; ++j) {
+            s[j] = exp(s[j] - m);
+            denom += s[j];
+          }
+          for (int32_t c = 0; c < head_dim; ++c) o[c] = 0.0;
+          for (int32_t j = 0; j <= p; ++j) {
+            const double wj = s[j] / denom;
+            for (int32_t c = 0; c < head_dim; ++c) o[c] += wj * Vr[(int64_t)j * head_dim + c];
+          }
+        }
+      }
+    }
+    free(Kr); free(Vr); free(s);
+  }
+  free(items);
+  free(sel);
+  return status;
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

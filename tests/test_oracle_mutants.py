@@ -1,0 +1,71 @@
+"""The oracle's pins have teeth: plausible mistakes planted in copies of
+oracle.c (on the CPU only) must each make the pin suite fail.
+
+Each mutant is one small textual change -- a dropped term, an off-by-one, a
+wrong sign, a wrong index, a transposed layout -- compiled to a temporary
+library that the pin suite then loads in a subprocess.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "positions drop computed tokens": ("const int32_t pos = nct[r] + t;", "const int32_t pos = t;"),
+    "slot drops block size factor": ("(int64_t)phys * block_size + pos % block_size",
+                                     "(int64_t)phys + pos % block_size"),
+    "slot uses logical block": ("const int32_t phys = block_table[(int64_t)r * bt_stride + logical];",
+                                "const int32_t phys = logical;"),
+    "logits index off by one": ("logits_indices[r] = qsl[r + 1] - 1;", "logits_indices[r] = qsl[r + 1];"),
+    "qsl tail not padded": ("qsl[k] = total;", "qsl[k] = 0;"),
+    "seq_lens drop scheduled": ("seq_lens[r] = nct[r] + nst[r];", "seq_lens[r] = nct[r];"),
+    "causal top-left alignment": ("const int32_t p = L - q_len + (row - qsl[r]);",
+                                  "const int32_t p = (row - qsl[r]);"),
+    "causal excludes diagonal": ("for (int32_t j = 0; j <= p; ++j) {\n            double acc",
+                                 "for (int32_t j = 0; j < p; ++j) {\n            double acc"),
+    "scale dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "softmax sign flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    "gqa interleaved heads": ("for (int32_t h = g * group; h < (g + 1) * group; ++h) {",
+                              "for (int32_t h = g; h < num_q_heads; h += num_kv_heads) {"),
+    "value layout transposed": ("return ((block * num_kv_heads + head) * (int64_t)head_dim + dim) * block_size + tok;",
+                                "return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;"),
+    "gather offset uses block index": ("const int32_t off = j % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          Kr",
+                                       "const int32_t off = (j / block_size) % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          Kr"),
+    "kv write uses key layout for values": (
+        "const int64_t dv = orc_v_elem(block, h, off, c, num_kv_heads, block_size, head_dim);",
+        "const int64_t dv = orc_k_elem(block, h, off, c, num_kv_heads, block_size, head_dim);"),
+    "bf16 widening wrong half": ("uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;",
+                                 "uint32_t bits = (uint32_t)((const uint16_t*)base)[idx];"),
+    "normaliser dropped": ("const double wj = s[j] / denom;", "const double wj = s[j];"),
+}
+
+
+def _run_mutant(name, find, repl, tmp):
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation site for {name!r} not unique/found"
+    path_c = os.path.join(tmp, f"m{abs(hash(name))}.c")
+    path_so = path_c[:-2] + ".so"
+    with open(path_c, "w") as f:
+        f.write(src.replace(find, repl))
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", path_c, "-o",
+                    path_so, "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, ORACLE_LIB_OVERRIDE=path_so, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    return name, r.returncode
+
+
+def test_every_planted_mistake_fails_a_pin():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=4) as ex:
+            futs = [ex.submit(_run_mutant, n, f, r, tmp) for n, (f, r) in MUTANTS.items()]
+            results = dict(f.result() for f in futs)
+    survivors = [n for n, rc in results.items() if rc == 0]
+    assert not survivors, f"mutants not caught by any pin: {survivors}"

@@ -1,0 +1,454 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle is checked against things other than itself:
+  * values the pages print (tests/golden/prepare_page_examples.json, each entry
+    cited to its page and section);
+  * torch's own fp64 scaled-dot-product attention over the whole unpaged
+    sequence (a library routine the oracle does not call), which also fixes
+    the causal alignment of a chunk that starts mid-sequence and the GQA head
+    grouping;
+  * closed forms (two-key softmax, all-ones V, zero Q, position-0 rows);
+  * invariants (block-permutation and request-permutation invariance, padding
+    of query_start_loc, uniqueness of slots).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "prepare_page_examples.json")
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _table(rows, width=None):
+    width = width or max(len(r) for r in rows)
+    t = np.full((len(rows), width), -1, np.int32)
+    for i, r in enumerate(rows):
+        t[i, :len(r)] = r
+    return t
+
+
+# ---------------------------------------------------------------------------
+# prepare
+# ---------------------------------------------------------------------------
+
+def test_prepare_worked_example_253(golden):
+    g = golden["worked_example_253"]
+    nst = g["num_scheduled_tokens"]
+    bt = _table([[0], [1], [2]])
+    out = oracle.prepare(nst, [0, 0, 0], bt, block_size=16, num_blocks=3)
+    assert out["req_indices"].tolist() == g["req_indices"]
+    assert out["query_start_loc"][1:].tolist() == g["cu_num_tokens"]
+    # with nothing computed yet a token's position is its offset in the chunk
+    assert out["positions"].tolist() == g["query_pos"]
+    assert out["query_start_loc"].tolist() == g["query_start_loc"]
+    assert out["logits_indices"].tolist() == g["logits_indices"]
+
+
+def test_prepare_positions_add_computed_tokens(golden):
+    # "A token's position is its request's num_computed_tokens plus its offset
+    # within this step's chunk" (Building the Batch, "How they are computed").
+    g = golden["worked_example_253"]
+    nct = [14, 0, 9]
+    bt = _table([[5], [3], [9]])
+    out = oracle.prepare(g["num_scheduled_tokens"], nct, bt, block_size=16, num_blocks=16)
+    qpos = np.array(g["query_pos"])
+    req = np.array(g["req_indices"])
+    assert out["positions"].tolist() == (np.array(nct)[req] + qpos).tolist()
+    assert out["seq_lens"].tolist() == [16, 5, 12]
+
+
+def test_prepare_packed_batch_411(golden):
+    g = golden["packed_batch_411"]
+    bt = _table([[0], [1, 2, 3, 4], [5, 6]])
+    out = oracle.prepare(g["num_scheduled_tokens"], g["num_computed_tokens"], bt,
+                         block_size=16, num_blocks=8)
+    assert out["positions"].tolist() == g["positions"]
+    assert out["query_start_loc"].tolist() == g["query_start_loc"]
+
+
+def test_prepare_go_program_hand_checked_slots(golden):
+    g = golden["go_program_bs4"]
+    bt = _table(g["block_tables"])
+    out = oracle.prepare(g["num_scheduled_tokens"], g["num_computed_tokens"], bt,
+                         block_size=g["block_size"], num_blocks=16)
+    rows_b = np.nonzero(out["req_indices"] == 1)[0]
+    assert out["positions"][rows_b].tolist() == g["request_B_positions"]
+    assert out["slot_mapping"][rows_b].tolist() == g["request_B_slots"]
+
+
+def test_prepare_nano_block_mapping(golden):
+    g = golden["nano_block_mapping"]
+    bs = g["block_size"]
+    out = oracle.prepare([10], [0], _table([g["block_table"]]), block_size=bs, num_blocks=16)
+    slots = out["slot_mapping"]
+    assert (slots // bs).tolist() == g["token_physical_block"]
+    assert (slots % bs).tolist() == g["token_in_block_order"]
+
+
+def test_prepare_hand_derived_exercises(golden):
+    h = golden["hand_derived"]
+    q2 = h["check_yourself_q2"]
+    # a single decode token at position 37
+    out = oracle.prepare([1], [q2["position"]], _table([q2["block_table"]]),
+                         block_size=q2["block_size"], num_blocks=64)
+    assert out["slot_mapping"].tolist() == [q2["slot"]]
+    t1 = h["try_it_q1"]
+    out = oracle.prepare([t1["num_scheduled_tokens"]], [t1["num_computed_tokens"]],
+                         _table([t1["block_table"]]), block_size=t1["block_size"], num_blocks=16)
+    assert out["slot_mapping"].tolist() == t1["slots"]
+
+
+def test_prepare_new_block_exactly_at_boundary():
+    # nano-vLLM section 2.6: a decode step needs a fresh block exactly when
+    # len(seq) % block_size == 1, i.e. the new token is the first of a block.
+    bs = 16
+    lens = np.arange(1, 100)
+    nct = lens - 1
+    R = len(lens)
+    need = (lens + bs - 1) // bs
+    bt = np.full((R, need.max()), -1, np.int32)
+    for r in range(R):
+        bt[r, :need[r]] = 1000 + 10 * r + np.arange(need[r])
+    out = oracle.prepare(np.ones(R), nct, bt, block_size=bs, num_blocks=10_000)
+    first_of_block = (out["slot_mapping"] % bs) == 0
+    assert first_of_block.tolist() == ((lens % bs) == 1).tolist()
+    # and the block it lands in is the request's last table entry
+    assert (out["slot_mapping"] // bs).tolist() == [bt[r, need[r] - 1] for r in range(R)]
+
+
+def test_prepare_query_start_loc_tail_padding():
+    # "the unused tail is filled with the total so that every request beyond
+    # the real ones has zero length" (Building the Batch, "How they are computed")
+    out = oracle.prepare([3, 1, 4], [0, 7, 2], _table([[0], [1], [2]]), block_size=16,
+                         num_blocks=3, qsl_len=9)
+    qsl = out["query_start_loc"]
+    assert qsl.tolist() == [0, 3, 4, 8, 8, 8, 8, 8, 8]
+    assert np.all(np.diff(qsl) >= 0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prepare_random_matches_vectorised_form_and_invariants(seed):
+    """Loop oracle vs the pages' vectorised NumPy form (np.repeat / cumsum /
+    fancy indexing, as printed in "How they are computed"), plus invariants."""
+    rng = np.random.default_rng(seed)
+    R = int(rng.integers(1, 12))
+    bs = int(rng.choice([1, 4, 16]))
+    nst = rng.integers(0, 40, size=R).astype(np.int32)
+    nct = rng.integers(0, 70, size=R).astype(np.int32)
+    seq = nst + nct
+    need = (seq + bs - 1) // bs
+    nb = int(need.sum()) + 5
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((R, max(int(need.max()), 1) + 2), -1, np.int32)
+    c = 0
+    for r in range(R):
+        bt[r, :need[r]] = perm[c:c + need[r]]
+        c += need[r]
+    out = oracle.prepare(nst, nct, bt, block_size=bs, num_blocks=nb, qsl_len=R + 3)
+    T = int(nst.sum())
+
+    req = np.repeat(np.arange(R), nst)
+    cu = np.cumsum(nst)
+    query_pos = np.arange(T) - np.repeat(cu - nst, nst)
+    pos = nct[req] + query_pos
+    slots = bt[req, pos // bs].astype(np.int64) * bs + pos % bs
+    assert out["req_indices"].tolist() == req.tolist()
+    assert out["positions"].tolist() == pos.tolist()
+    assert out["slot_mapping"].tolist() == slots.tolist()
+    assert out["query_start_loc"].tolist() == [0] + cu.tolist() + [T, T]
+    assert out["seq_lens"].tolist() == seq.tolist()
+    # invariants
+    qsl = out["query_start_loc"]
+    assert qsl[R] == T
+    assert np.all(out["positions"] < out["seq_lens"][out["req_indices"]])
+    q_len = qsl[1:R + 1] - qsl[:R]
+    r_of = out["req_indices"]
+    t = np.arange(T) - qsl[r_of]
+    assert np.all(out["positions"] == out["seq_lens"][r_of] - q_len[r_of] + t)
+    assert len(set(out["slot_mapping"].tolist())) == T  # disjoint tables -> unique slots
+
+
+def test_prepare_rejects_out_of_range_blocks():
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.prepare([2], [15], _table([[0]]), block_size=16, num_blocks=4)
+    assert e.value.code == oracle.ERR_RANGE  # position 16 needs a second table column
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.prepare([1], [0], _table([[9]]), block_size=16, num_blocks=4)
+    assert e.value.code == oracle.ERR_RANGE
+
+
+def test_prepare_empty_batch():
+    out = oracle.prepare(np.zeros(0, np.int32), np.zeros(0, np.int32),
+                         np.zeros((0, 1), np.int32), block_size=16, num_blocks=1, qsl_len=4)
+    assert out["query_start_loc"].tolist() == [0, 0, 0, 0]
+    assert out["slot_mapping"].size == 0
+
+
+# ---------------------------------------------------------------------------
+# kv_write
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_kv_write_post_state(dtype):
+    g = torch.Generator().manual_seed(3)
+    nb, H, bs, d, T = 7, 3, 4, 8, 9
+    kc = torch.randn(nb, H, bs, d, generator=g).to(dtype)
+    vc = torch.randn(nb, H, d, bs, generator=g).to(dtype)
+    key = torch.randn(T, H, d, generator=g).to(dtype)
+    val = torch.randn(T, H, d, generator=g).to(dtype)
+    slots = torch.randperm(nb * bs, generator=g)[:T].numpy().astype(np.int64)
+    slots[4] = -1  # padding row: no write
+    kc0, vc0 = kc.clone(), vc.clone()
+    oracle.kv_write(key, val, kc, vc, slots, block_size=bs)
+    written = np.zeros((nb, bs), bool)
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        b, o = divmod(int(s), bs)
+        written[b, o] = True
+        assert torch.equal(kc[b, :, o, :], key[i])
+        assert torch.equal(vc[b, :, :, o], val[i])
+    keep = torch.from_numpy(~written)
+    assert torch.equal(kc[keep[:, None, :, None].expand_as(kc)],
+                       kc0[keep[:, None, :, None].expand_as(kc0)])
+    assert torch.equal(vc[keep[:, None, None, :].expand_as(vc)],
+                       vc0[keep[:, None, None, :].expand_as(vc0)])
+
+
+def test_kv_write_rejects_duplicates_and_range():
+    kc = torch.zeros(2, 1, 4, 8)
+    vc = torch.zeros(2, 1, 8, 4)
+    k = torch.ones(2, 1, 8)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.kv_write(k, k, kc, vc, [3, 3], block_size=4)
+    assert e.value.code == oracle.ERR_DUP
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.kv_write(k, k, kc, vc, [3, 8], block_size=4)
+    assert e.value.code == oracle.ERR_RANGE
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def make_paged(nst, nct, Hq, Hkv, d, bs, seed, dtype=torch.float32, slack=3):
+    """Contiguous per-request K/V/Q first, then the same rows placed into a
+    NaN-filled paged pool at random blocks.  Returns (logical, paged)."""
+    rng = np.random.default_rng(seed)
+    g = torch.Generator().manual_seed(seed)
+    nst = np.asarray(nst, np.int32)
+    nct = np.asarray(nct, np.int32)
+    R = len(nst)
+    L = nst + nct
+    need = (L + bs - 1) // bs
+    nb = int(need.sum()) + slack
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((R, int(need.max()) + 1), -1, np.int32)
+    c = 0
+    for r in range(R):
+        bt[r, :need[r]] = perm[c:c + need[r]]
+        c += need[r]
+    Ks = [torch.randn(int(L[r]), Hkv, d, generator=g).to(dtype) for r in range(R)]
+    Vs = [torch.randn(int(L[r]), Hkv, d, generator=g).to(dtype) for r in range(R)]
+    Qs = [torch.randn(int(L[r]), Hq, d, generator=g).to(dtype) for r in range(R)]
+    kc = torch.full((nb, Hkv, bs, d), float("nan"), dtype=dtype)
+    vc = torch.full((nb, Hkv, d, bs), float("nan"), dtype=dtype)
+    for r in range(R):
+        for j in range(int(L[r])):
+            b, o = int(bt[r, j // bs]), j % bs
+            kc[b, :, o, :] = Ks[r][j]
+            vc[b, :, :, o] = Vs[r][j]
+    q = torch.cat([Qs[r][int(nct[r]):] for r in range(R)]).contiguous()
+    qsl = np.concatenate([[0], np.cumsum(nst)]).astype(np.int32)
+    return dict(Ks=Ks, Vs=Vs, Qs=Qs, nst=nst, nct=nct), dict(
+        q=q, kc=kc, vc=vc, qsl=qsl, seq_lens=L.astype(np.int32), bt=bt, bs=bs)
+
+
+def sdpa_reference(logical, scale):
+    """torch fp64 SDPA over each whole sequence (is_causal on the square
+    L x L problem), keeping the rows of this step's chunk."""
+    outs = []
+    for Qr, Kr, Vr, n, c in zip(logical["Qs"], logical["Ks"], logical["Vs"],
+                                logical["nst"], logical["nct"]):
+        if n == 0:
+            continue
+        o = F.scaled_dot_product_attention(
+            Qr.double().transpose(0, 1)[None], Kr.double().transpose(0, 1)[None],
+            Vr.double().transpose(0, 1)[None], is_causal=True, scale=scale, enable_gqa=True)
+        outs.append(o[0].transpose(0, 1)[int(c):])
+    return torch.cat(outs).numpy()
+
+
+def run_oracle(paged, scale, rows=None):
+    return oracle.attention(paged["q"], paged["kc"], paged["vc"], paged["qsl"],
+                            paged["seq_lens"], paged["bt"], paged["bs"], scale, rows=rows)
+
+
+CASES = [
+    # (nst, nct, Hq, Hkv, d, bs)
+    ([1, 1, 1], [0, 5, 40], 4, 4, 16, 4),               # decodes incl. a position-0 token
+    ([7, 1, 3], [0, 19, 9], 4, 2, 8, 4),                # fresh prefill, decode, chunk mid-seq
+    ([2, 5, 3], [14, 0, 9], 4, 2, 64, 16),              # the worked-example shape
+    ([33, 1, 0, 2], [17, 64, 5, 0], 8, 2, 32, 16),      # GQA 4, empty request, ragged
+    ([5], [60], 6, 1, 16, 8),                           # MQA
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_attention_matches_torch_sdpa(case):
+    nst, nct, Hq, Hkv, d, bs = CASES[case]
+    logical, paged = make_paged(nst, nct, Hq, Hkv, d, bs, seed=10 + case)
+    scale = 1.0 / math.sqrt(d)
+    ref = sdpa_reference(logical, scale)
+    got = run_oracle(paged, scale)
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_scale_is_applied():
+    logical, paged = make_paged([3, 1], [4, 9], 2, 2, 16, 4, seed=5)
+    for scale in (0.05, 0.7):
+        assert np.max(np.abs(run_oracle(paged, scale) - sdpa_reference(logical, scale))) < 1e-12
+
+
+def test_attention_bf16_inputs_widen_exactly():
+    logical, paged = make_paged([3, 1], [5, 30], 4, 2, 32, 16, seed=6, dtype=torch.bfloat16)
+    scale = 0.125
+    ref = sdpa_reference(logical, scale)   # bf16 values upcast exactly to fp64
+    assert np.max(np.abs(run_oracle(paged, scale) - ref)) < 1e-12
+
+
+def test_attention_two_key_closed_form():
+    # one request, 2 tokens of history + 1 new token at position 2; head_dim 1
+    # keys 0, 1, 2 with k = [1, 2, -1], q = 0.5, v = [10, 20, 30], scale 1
+    # -> weights exp(0.5), exp(1.0), exp(-0.5) (closed form written out)
+    kc = torch.full((1, 1, 4, 1), float("nan"))
+    vc = torch.full((1, 1, 1, 4), float("nan"))
+    kc[0, 0, :3, 0] = torch.tensor([1.0, 2.0, -1.0])
+    vc[0, 0, 0, :3] = torch.tensor([10.0, 20.0, 30.0])
+    q = torch.tensor([[[0.5]]])
+    out = oracle.attention(q, kc, vc, [0, 1], [3], np.array([[0]]), 4, 1.0)
+    w = np.exp([0.5, 1.0, -0.5])
+    expect = (w @ np.array([10.0, 20.0, 30.0])) / w.sum()
+    assert abs(out[0, 0, 0] - expect) < 1e-12
+
+
+def test_attention_block_permutation_invariance():
+    logical, paged = make_paged([6, 1, 2], [10, 33, 0], 4, 2, 16, 4, seed=7, slack=6)
+    base = run_oracle(paged, 0.25)
+    rng = np.random.default_rng(1)
+    nb = paged["kc"].shape[0]
+    perm = rng.permutation(nb)          # new position of old block b is perm[b]
+    kc2 = torch.empty_like(paged["kc"])
+    vc2 = torch.empty_like(paged["vc"])
+    kc2[torch.from_numpy(perm)] = paged["kc"]
+    vc2[torch.from_numpy(perm)] = paged["vc"]
+    bt2 = np.where(paged["bt"] >= 0, perm[np.maximum(paged["bt"], 0)], -1).astype(np.int32)
+    moved = dict(paged, kc=kc2, vc=vc2, bt=bt2)
+    assert np.array_equal(run_oracle(moved, 0.25), base)   # bit-exact
+
+
+def test_attention_request_permutation_permutes_rows():
+    nst, nct = [3, 1, 2], [2, 20, 7]
+    logical, paged = make_paged(nst, nct, 4, 2, 16, 4, seed=8)
+    base = run_oracle(paged, 0.3)
+    order = [2, 0, 1]
+    qsl = paged["qsl"]
+    row_blocks = [np.arange(qsl[r], qsl[r + 1]) for r in range(3)]
+    new_rows = np.concatenate([row_blocks[r] for r in order])
+    new_nst = np.array(nst)[order]
+    moved = dict(paged, q=paged["q"][torch.from_numpy(new_rows)].contiguous(),
+                 qsl=np.concatenate([[0], np.cumsum(new_nst)]).astype(np.int32),
+                 seq_lens=paged["seq_lens"][order], bt=paged["bt"][order])
+    assert np.array_equal(run_oracle(moved, 0.3), base[new_rows])
+
+
+def test_attention_softmax_rows_sum_to_one():
+    logical, paged = make_paged([4, 1], [3, 50], 4, 2, 16, 4, seed=9)
+    ones_v = torch.where(torch.isnan(paged["vc"]), paged["vc"], torch.ones_like(paged["vc"]))
+    out = oracle.attention(paged["q"], paged["kc"], ones_v, paged["qsl"], paged["seq_lens"],
+                           paged["bt"], paged["bs"], 0.5)
+    assert np.max(np.abs(out - 1.0)) < 1e-14
+
+
+def test_attention_position_zero_returns_first_value():
+    logical, paged = make_paged([5], [0], 2, 1, 16, 4, seed=11)
+    out = run_oracle(paged, 0.25)
+    v0 = logical["Vs"][0][0, 0].double().numpy()
+    assert np.array_equal(out[0, 0], v0) and np.array_equal(out[0, 1], v0)
+
+
+def test_attention_zero_query_averages_visible_values():
+    logical, paged = make_paged([3, 1], [4, 12], 2, 2, 8, 4, seed=12)
+    zq = dict(paged, q=torch.zeros_like(paged["q"]))
+    out = run_oracle(zq, 0.7)
+    row = 0
+    for r in range(2):
+        for t in range(int(logical["nst"][r])):
+            p = int(logical["nct"][r]) + t
+            mean = logical["Vs"][r][:p + 1].double().mean(0).numpy()   # [Hkv, d]
+            assert np.max(np.abs(out[row] - mean)) < 1e-14
+            row += 1
+
+
+def test_attention_gqa_equals_mha_on_repeated_kv():
+    nst, nct = [2, 1], [5, 9]
+    logical, paged = make_paged(nst, nct, 6, 2, 8, 4, seed=13)
+    gqa = run_oracle(paged, 0.4)
+    rep = dict(paged, kc=paged["kc"].repeat_interleave(3, dim=1).contiguous(),
+               vc=paged["vc"].repeat_interleave(3, dim=1).contiguous())
+    mha = run_oracle(rep, 0.4)
+    assert np.array_equal(gqa, mha)
+
+
+def test_attention_row_subset_matches_full():
+    logical, paged = make_paged([6, 1, 4], [3, 40, 0], 4, 2, 16, 4, seed=14)
+    full = run_oracle(paged, 0.25)
+    rows = np.array([10, 0, 7, 3])
+    assert np.array_equal(run_oracle(paged, 0.25, rows=rows), full[rows])
+
+
+def test_attention_rejects_bad_inputs():
+    logical, paged = make_paged([2], [3], 2, 1, 8, 4, seed=15)
+    with pytest.raises(oracle.OracleError) as e:   # q_len > seq_len
+        oracle.attention(paged["q"], paged["kc"], paged["vc"], [0, 2], [1], paged["bt"], 4, 1.0)
+    assert e.value.code == oracle.ERR_PRECOND
+    bad = paged["bt"].copy()
+    bad[0, 0] = 999
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.attention(paged["q"], paged["kc"], paged["vc"], paged["qsl"], paged["seq_lens"],
+                         bad, 4, 1.0)
+    assert e.value.code == oracle.ERR_RANGE
+
+
+def test_prepare_write_attention_chain_equals_unpaged_sdpa():
+    """The three oracle steps chained the way one step of the hot path runs:
+    prepare -> write the new rows at slot_mapping -> attention."""
+    nst, nct = np.array([3, 1, 5], np.int32), np.array([6, 21, 0], np.int32)
+    logical, paged = make_paged(nst, nct, 4, 2, 16, 4, seed=16)
+    R = len(nst)
+    # wipe this step's slots, then let prepare + kv_write put them back
+    kc, vc = paged["kc"].clone(), paged["vc"].clone()
+    key = torch.cat([logical["Ks"][r][nct[r]:] for r in range(R)]).contiguous()
+    val = torch.cat([logical["Vs"][r][nct[r]:] for r in range(R)]).contiguous()
+    prep = oracle.prepare(nst, nct, paged["bt"], block_size=4, num_blocks=kc.shape[0])
+    for s in prep["slot_mapping"]:
+        kc[s // 4, :, s % 4, :] = float("nan")
+        vc[s // 4, :, :, s % 4] = float("nan")
+    oracle.kv_write(key, val, kc, vc, prep["slot_mapping"], block_size=4)
+    out = oracle.attention(paged["q"], kc, vc, prep["query_start_loc"], prep["seq_lens"],
+                           paged["bt"], 4, 0.25)
+    assert np.max(np.abs(out - sdpa_reference(logical, 0.25))) < 1e-12

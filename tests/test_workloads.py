@@ -1,0 +1,48 @@
+"""The seeded input generator builds what the configurations say (no GPU)."""
+import numpy as np
+import torch
+
+from paged_kv_cache_prepare_amd import workloads
+
+
+def test_config1_structure_and_poison():
+    wl = workloads.config(1)
+    assert wl.num_scheduled_tokens.tolist() == [2, 5, 3]
+    assert wl.num_computed_tokens.tolist() == [14, 0, 9]
+    assert wl.num_blocks == 16 and wl.block_size == 16
+    assert (wl.num_q_heads, wl.num_kv_heads, wl.head_dim) == (4, 2, 64)
+    assert wl.dtype == torch.float32 and abs(wl.scale - 0.125) < 1e-15
+    used = wl.block_table[wl.block_table >= 0]
+    assert len(used) == 3 and len(set(used.tolist())) == 3
+    # history slots are finite, everything else in the pool is NaN
+    hist = int(np.isfinite(wl.key_cache[:, 0, :, 0].numpy()).sum())
+    assert hist == 14 + 0 + 9
+    assert torch.isnan(wl.value_cache).sum() == (16 * 16 - 23) * 2 * 64
+    assert wl.q.shape == (10, 4, 64) and torch.isfinite(wl.q).all()
+
+
+def test_same_seed_same_inputs():
+    a, b = workloads.config(1), workloads.config(1)
+    assert np.array_equal(a.block_table, b.block_table)
+    assert torch.equal(a.q, b.q) and torch.equal(a.key, b.key)
+
+
+def test_shared_prefix_groups_share_physical_blocks():
+    wl = workloads.build("t", [1, 1, 1, 2], [63, 63, 40, 0], num_q_heads=4, num_kv_heads=2,
+                         head_dim=8, seed=3, shared_prefix_groups=[([0, 1], 32)])
+    bt = wl.block_table
+    assert np.array_equal(bt[0, :2], bt[1, :2])
+    assert bt[0, 2] != bt[1, 2] and bt[0, 3] != bt[1, 3]
+    rest = np.concatenate([bt[0, :4], bt[1, 2:4], bt[2, :3], bt[3, :1]])
+    assert len(set(rest.tolist())) == len(rest)
+    assert wl.notes["shared_blocks"] == 2
+
+
+def test_large_config_structures():
+    s4 = workloads.config_structure(4)
+    assert s4["num_scheduled_tokens"].sum() == 5200 and len(s4["num_scheduled_tokens"]) == 201
+    ctx = s4["num_computed_tokens"][1:] + 1
+    assert ctx.min() >= 1024 and ctx.max() <= 8192
+    s5 = workloads.config_structure(5)
+    assert s5["num_scheduled_tokens"].sum() == 2064
+    assert (s5["num_computed_tokens"][:16] + 1 == 32768).all()
