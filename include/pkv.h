@@ -1,0 +1,231 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged KV-cache input preparation, KV-cache write
+ * and paged variable-length causal attention for AMD Instinct MI355X (gfx950).
+ *
+ * One step of paged LLM serving runs three calls, in this order, on one HIP
+ * stream:
+ *
+ *   pkv_prepare_inputs         flat-batch index tensors from the scheduler's
+ *                              per-request token counts and block tables;
+ *   pkv_kv_cache_write         each new token's K and V rows into the block
+ *                              pool at its slot;
+ *   pkv_paged_attention_varlen causal attention of every query row of the
+ *                              step (prefill chunks and single-token decodes
+ *                              alike, in one launch) over its request's
+ *                              context, read through the block table.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device pointers must be device memory (or memory the
+ *   device can address) owned by the caller.  The library allocates nothing,
+ *   keeps no device state between calls, never synchronises, never reads
+ *   device memory from the host, and only enqueues work on `stream`
+ *   (a hipStream_t; NULL means the default stream).  Calls are reentrant.
+ * - Host-side validation covers the scalar arguments and null pointers only;
+ *   it returns a status and enqueues nothing on failure.  Device-side
+ *   contents are preconditions (listed per call).  Where a precondition on
+ *   device data is broken the kernels still never touch memory outside the
+ *   buffers described here; the affected outputs are then unspecified.
+ * - Integer index tensors are int32 except slot_mapping (int64, -1 = no
+ *   write).  Block pools are two separate tensors:
+ *     K pool: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major)
+ *     V pool: [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major)
+ *   The pages leave the cache layout to the kernel ("Inside vLLM: Following
+ *   One Request from the API to GPU Execution", Part 5, which notes that
+ *   different write/read kernel pairs use different layouts).  A dim-major V
+ *   block makes the P.V contraction over tokens read 16 consecutive tokens
+ *   of one dimension as one contiguous run.
+ * - Ordering: the KV write of a step must be enqueued before the attention
+ *   that reads it, on the same stream or behind an event.  The pages make the
+ *   same requirement explicit with a dummy data dependency ("Inside vLLM...",
+ *   Part 4).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes  */
+  PKV_ERR_UNSUPPORTED = 2, /* a valid argument this build has no kernel for    */
+  PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  PKV_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch         */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,  /* IEEE binary32                                   */
+  PKV_BF16 = 1  /* bfloat16 (top 16 bits of binary32); fp32 accumulate */
+} pkv_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* pkv_status_string(pkv_status status);
+
+/*
+ * pkv_prepare_inputs -- flat-batch index tensors for one step.
+ *
+ * Follows "Building the Batch", sections "How they are computed" and
+ * "Reading and writing the KV cache", and "vLLM's Model Runner -- the
+ * Persistent Batch, in Source", "The two things this method returns".  With
+ * nst = num_scheduled_tokens, nct = num_computed_tokens, for request r:
+ *   query_start_loc[0] = 0, query_start_loc[r+1] = query_start_loc[r] + nst[r]
+ *   seq_lens[r]        = nct[r] + nst[r]
+ *   logits_indices[r]  = query_start_loc[r+1] - 1
+ * and for the t-th scheduled token of r, at flat row i = query_start_loc[r] + t:
+ *   req_indices[i]  = r
+ *   positions[i]    = nct[r] + t
+ *   slot_mapping[i] = block_table[r][positions[i] / block_size] * block_size
+ *                     + positions[i] % block_size
+ * query_start_loc[num_reqs+1 .. qsl_len-1] = the token total, so the array is
+ * non-decreasing and padding "requests" have an empty row range.
+ *
+ * Arguments (device pointers unless stated):
+ *   num_scheduled_tokens, num_computed_tokens  int32 [num_reqs], >= 0
+ *   block_table     int32 [num_reqs][bt_row_stride]; a request reads only
+ *                   columns < bt_row_stride
+ *   num_reqs        host, >= 0;  num_tokens host, = sum(num_scheduled_tokens)
+ *   qsl_len         host, >= num_reqs + 1
+ *   block_size      host, >= 1
+ *   num_blocks      host, size of the block pool; slots are checked against it
+ *   req_indices, positions  int32 [num_tokens]  (out)
+ *   slot_mapping    int64 [num_tokens]          (out)
+ *   query_start_loc int32 [qsl_len]             (out)
+ *   seq_lens, logits_indices int32 [num_reqs]   (out)
+ * Device-data behaviour: a token whose block-table column is >= bt_row_stride
+ * or whose block id is outside [0, num_blocks) gets slot -1 (no write).  If
+ * sum(num_scheduled_tokens) differs from num_tokens, rows past the device sum
+ * get req_indices = positions = -1 and slot -1.
+ * Errors: PKV_ERR_INVALID_ARG for null pointers (outputs of size 0 may be
+ * NULL), negative sizes, qsl_len < num_reqs + 1, block_size < 1,
+ * bt_row_stride < 1 when num_tokens > 0; PKV_ERR_LAUNCH.
+ */
+pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
+                              const int32_t* num_computed_tokens, const int32_t* block_table,
+                              int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens,
+                              int32_t qsl_len, int32_t block_size, int64_t num_blocks,
+                              int32_t* req_indices, int32_t* positions, int64_t* slot_mapping,
+                              int32_t* query_start_loc, int32_t* seq_lens,
+                              int32_t* logits_indices, void* stream);
+
+/*
+ * pkv_kv_cache_write -- scatter this step's K and V rows into the block pool.
+ *
+ * Follows "Inside vLLM: Following One Request from the API to GPU Execution",
+ * Part 5: for token i the K and V vectors go to the cache slot
+ * slot_mapping[i] = physical_block * block_size + in_block_offset; the write
+ * is token-granular while reads are block-granular.  For every i with
+ * s = slot_mapping[i] in [0, num_blocks * block_size) and every kv head h:
+ *   K pool[s / block_size][h][s % block_size][:] = key[i][h][:]
+ *   V pool[s / block_size][h][:][s % block_size] = value[i][h][:]
+ * Bytes are copied unchanged.  Slots < 0 (padding rows) and slots past the
+ * pool are skipped.
+ *
+ * Arguments (device pointers unless stated):
+ *   key, value      [num_tokens][num_kv_heads][head_dim] of `dtype`; row i
+ *                   starts at element i * key_row_stride (value_row_stride);
+ *                   heads and dims are contiguous within a row; row starts
+ *                   must be 16-byte aligned
+ *   key_cache, value_cache  the K and V pools (layouts above), 16-byte aligned
+ *   num_blocks      host, blocks in each pool
+ *   slot_mapping    int64 [num_tokens]
+ *   num_tokens, num_kv_heads, head_dim, block_size   host
+ *   dtype           PKV_F32 or PKV_BF16
+ * Preconditions: slots are unique within a call (two tokens with the same slot
+ * leave either row there).
+ * Errors: PKV_ERR_INVALID_ARG (null pointers with num_tokens > 0, sizes < 1,
+ * row strides < num_kv_heads * head_dim); PKV_ERR_UNSUPPORTED when
+ * head_dim * element size is not a multiple of 16 bytes or head_dim > 256;
+ * PKV_ERR_LAUNCH.
+ */
+pkv_status pkv_kv_cache_write(const void* key, const void* value, int64_t key_row_stride,
+                              int64_t value_row_stride, void* key_cache, void* value_cache,
+                              int64_t num_blocks, const int64_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_paged_attention_workspace_bytes -- device workspace that
+ * pkv_paged_attention_varlen needs for these host-side sizes (the work list
+ * and, for long decode contexts split into partitions, the per-partition
+ * partial results).  The arguments mean what they mean there; split_tokens = 0
+ * selects the library's own partition size.  Returns 0 for invalid sizes.
+ */
+size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_query_len,
+                                           int32_t max_seq_len, int32_t split_tokens,
+                                           pkv_dtype dtype);
+
+/*
+ * pkv_paged_attention_varlen -- causal attention over a flat, variable-length
+ * batch whose K/V history lives in a block-paged pool.
+ *
+ * Follows "How vLLM Works Internally: A Deep Dive", "How the Kernel Works"
+ * (look up the block table, fetch K from scattered blocks, scores, softmax,
+ * weighted sum of V) and "PagedAttention V1/V2" (a second pass that reduces
+ * per-partition partial softmax results, used here for long decode
+ * contexts); "Inside vLLM...", Part 5 (the read call takes the query, both
+ * pools, the output, query_start_loc as the query boundaries, seq_lens as the
+ * visible K length and the block table).  For request r with
+ * q_len = query_start_loc[r+1] - query_start_loc[r] and L = seq_lens[r], the
+ * query at flat row i = query_start_loc[r] + t sits at absolute position
+ * p = L - q_len + t and sees keys 0..p.  For q head h and kv head
+ * g = h / (num_q_heads / num_kv_heads):
+ *   out[i][h][:] = sum_{j<=p} softmax_j(scale * q[i][h] . K_r[j][g]) V_r[j][g][:]
+ * where K_r[j] / V_r[j] is token j % block_size of physical block
+ * block_table[r][j / block_size].  Rows of the same step that belong to long
+ * prompt chunks and to single-token decodes are handled by one launch.
+ *
+ * Arguments (device pointers unless stated):
+ *   q               [num_tokens][num_q_heads][head_dim] of `dtype`, row i at
+ *                   element i * q_row_stride, 16-byte aligned rows
+ *   key_cache, value_cache  the K and V pools, num_blocks blocks each
+ *   out             [num_tokens][num_q_heads][head_dim] of `dtype`, row stride
+ *                   out_row_stride elements, 16-byte aligned rows (written)
+ *   query_start_loc int32 [num_reqs + 1], non-decreasing, last = num_tokens
+ *   seq_lens        int32 [num_reqs]
+ *   block_table     int32 [num_reqs][bt_row_stride]; request r reads columns
+ *                   0 .. ceil(seq_lens[r] / block_size) - 1, all < bt_row_stride
+ *   num_reqs, num_tokens    host
+ *   max_query_len, max_seq_len  host upper bounds of the device values (they
+ *                   size the launch and the workspace)
+ *   num_q_heads, num_kv_heads  host; num_q_heads % num_kv_heads == 0
+ *   head_dim        host, 64 or 128
+ *   block_size      host, 16
+ *   scale           host, the softmax scale (1/sqrt(head_dim) for plain models)
+ *   dtype           PKV_BF16 (MFMA path) or PKV_F32 (fp32 vector path)
+ *   split_tokens    host, partition size (tokens) for splitting one long
+ *                   decode context over several workgroups; 0 = automatic;
+ *                   otherwise a positive multiple of 32
+ *   workspace, workspace_bytes  device scratch of at least
+ *                   pkv_paged_attention_workspace_bytes(...) bytes, 256-byte
+ *                   aligned; its contents on entry do not matter
+ * Preconditions: 1 <= q_len <= seq_len for every request with q_len > 0;
+ * block ids in range for every column a request reads.  A row that sees no key
+ * (only when seq_len < q_len) is written as zeros; a block id outside
+ * [0, num_blocks) contributes no keys.  bf16 output is the fp32 result
+ * rounded to nearest even.
+ * Errors: PKV_ERR_INVALID_ARG (null pointers, sizes, num_q_heads not a
+ * multiple of num_kv_heads, row strides too small, split_tokens not a
+ * multiple of 32); PKV_ERR_UNSUPPORTED (head_dim not 64/128, block_size not
+ * 16, more than 16 q heads per kv head); PKV_ERR_WORKSPACE; PKV_ERR_LAUNCH.
+ */
+pkv_status pkv_paged_attention_varlen(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, int32_t split_tokens, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

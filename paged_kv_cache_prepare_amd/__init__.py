@@ -1,1 +1,11 @@
-"""Paged KV-cache prepare + paged varlen attention for MI355X (gfx950)."""
+"""Paged KV-cache input preparation, KV-cache write and paged varlen attention
+for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libpkv.so`` (HIP kernels behind the C ABI declared in
+``include/pkv.h``); :mod:`.binding` marshals torch tensors into those calls.
+"""
+from .binding import (PkvError, attention_workspace_bytes, kv_cache_write, load,
+                      paged_attention, prepare_inputs)
+
+__all__ = ["PkvError", "attention_workspace_bytes", "kv_cache_write", "load",
+           "paged_attention", "prepare_inputs"]

@@ -1,0 +1,64 @@
+"""Build libpkv.so (HIP, gfx950) in-tree with hipcc.
+
+Every source under csrc/ is compiled to an object in parallel, then linked
+into ``paged_kv_cache_prepare_amd/libpkv.so``.  Packed-fp32 instructions are
+switched off for all device code (``-packed-fp32-ops``).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+SOURCES = ["api.hip", "prepare.hip", "kv_write.hip", "attention.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: libpkv needs the ROCm toolchain")
+
+
+def compile_flags(extra=()) -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", INCLUDE, "-I", CSRC, *extra]
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile and link libpkv.so.  Always rebuilds.  Returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+
+    def one(src):
+        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
+        cmd = [cc, *compile_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        if verbose and r.stderr.strip():
+            print(r.stderr)
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,178 @@
+"""Thin ctypes binding over libpkv.so (include/pkv.h).
+
+Argument marshalling only: tensors are passed as device pointers, sizes as
+host integers, and the current torch stream as the HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no Python or CPU
+fallback.  If the library is not built this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+EXPORTS = ("pkv_status_string", "pkv_prepare_inputs", "pkv_kv_cache_write",
+           "pkv_paged_attention_workspace_bytes", "pkv_paged_attention_varlen")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_prepare_inputs.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P, P, P, P, P]
+    lib.pkv_prepare_inputs.restype = ctypes.c_int
+    lib.pkv_kv_cache_write.argtypes = [P, P, i64, i64, P, P, i64, P, i32, i32, i32, i32,
+                                       ctypes.c_int, P]
+    lib.pkv_kv_cache_write.restype = ctypes.c_int
+    lib.pkv_paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
+                                                        ctypes.c_int]
+    lib.pkv_paged_attention_workspace_bytes.restype = sz
+    lib.pkv_paged_attention_varlen.argtypes = [P, i64, P, P, i64, P, i64, P, P, P, i64, i32, i32,
+                                               i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
+                                               i32, P, sz, P]
+    lib.pkv_paged_attention_varlen.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pkv_status_string(int(status)).decode()
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _dev(t: torch.Tensor | None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise PkvError(status, what)
+
+
+def prepare_inputs(num_scheduled_tokens: torch.Tensor, num_computed_tokens: torch.Tensor,
+                   block_table: torch.Tensor, *, num_tokens: int, block_size: int,
+                   num_blocks: int, qsl_len: int | None = None, out: dict | None = None) -> dict:
+    """pkv_prepare_inputs.  ``num_tokens`` is the host-side token total."""
+    R = int(num_scheduled_tokens.shape[0])
+    dev = num_scheduled_tokens.device
+    qsl_len = R + 1 if qsl_len is None else int(qsl_len)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {"req_indices": torch.empty(num_tokens, **i32),
+               "positions": torch.empty(num_tokens, **i32),
+               "slot_mapping": torch.empty(num_tokens, dtype=torch.int64, device=dev),
+               "query_start_loc": torch.empty(qsl_len, **i32),
+               "seq_lens": torch.empty(R, **i32),
+               "logits_indices": torch.empty(R, **i32)}
+    assert block_table.dim() == 2 and (block_table.numel() == 0 or block_table.stride(1) == 1)
+    st = load().pkv_prepare_inputs(
+        _dev(num_scheduled_tokens, torch.int32, "num_scheduled_tokens"),
+        _dev(num_computed_tokens, torch.int32, "num_computed_tokens"),
+        _dev(block_table, torch.int32, "block_table"), max(1, block_table.stride(0)), R,
+        int(num_tokens),
+        qsl_len, int(block_size), int(num_blocks),
+        _dev(out["req_indices"], torch.int32), _dev(out["positions"], torch.int32),
+        _dev(out["slot_mapping"], torch.int64), _dev(out["query_start_loc"], torch.int32),
+        _dev(out["seq_lens"], torch.int32), _dev(out["logits_indices"], torch.int32),
+        _stream(dev))
+    _check(st, "pkv_prepare_inputs")
+    return out
+
+
+def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                   value_cache: torch.Tensor, slot_mapping: torch.Tensor, *,
+                   block_size: int) -> None:
+    """pkv_kv_cache_write.  key/value: [T, Hkv, d] with contiguous rows."""
+    T, H, d = key.shape
+    for t in (key, value):
+        assert t.stride(2) == 1 and t.stride(1) == d, "heads and dims must be contiguous"
+    assert key_cache.is_contiguous() and value_cache.is_contiguous()
+    st = load().pkv_kv_cache_write(
+        _dev(key, name="key"), _dev(value, name="value"), key.stride(0), value.stride(0),
+        _dev(key_cache, key.dtype, "key_cache"), _dev(value_cache, key.dtype, "value_cache"),
+        key_cache.shape[0], _dev(slot_mapping, torch.int64, "slot_mapping"), T, H, d,
+        int(block_size), _dtype_code(key.dtype), _stream(key.device))
+    _check(st, "pkv_kv_cache_write")
+
+
+def attention_workspace_bytes(num_reqs: int, num_tokens: int, num_q_heads: int,
+                              num_kv_heads: int, head_dim: int, max_query_len: int,
+                              max_seq_len: int, split_tokens: int = 0,
+                              dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load().pkv_paged_attention_workspace_bytes(
+        num_reqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len, max_seq_len,
+        split_tokens, _dtype_code(dtype)))
+
+
+def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                    query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+                    block_table: torch.Tensor, *, max_query_len: int, max_seq_len: int,
+                    scale: float | None = None, out: torch.Tensor | None = None,
+                    split_tokens: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """pkv_paged_attention_varlen.  q: [T, Hq, d]; pools: K [nb, Hkv, 16, d], V [nb, Hkv, d, 16]."""
+    T, Hq, d = q.shape
+    nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    R = int(seq_lens.shape[0])
+    assert q.stride(2) == 1 and q.stride(1) == d
+    assert key_cache.is_contiguous() and value_cache.is_contiguous()
+    assert block_table.dim() == 2 and block_table.stride(1) == 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    need = attention_workspace_bytes(R, T, Hq, Hkv, d, max_query_len, max_seq_len, split_tokens,
+                                     q.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, name="workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().pkv_paged_attention_varlen(
+        _dev(q, name="q"), q.stride(0), _dev(key_cache, q.dtype, "key_cache"),
+        _dev(value_cache, q.dtype, "value_cache"), nb, _dev(out, q.dtype, "out"), out.stride(0),
+        _dev(query_start_loc, torch.int32, "query_start_loc"),
+        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_table, torch.int32, "block_table"),
+        block_table.stride(0), R, T, int(max_query_len), int(max_seq_len), Hq, Hkv, d, bs,
+        float(scale), _dtype_code(q.dtype), int(split_tokens), ws_ptr, ws_bytes,
+        _stream(q.device))
+    _check(st, "pkv_paged_attention_varlen")
+    return out

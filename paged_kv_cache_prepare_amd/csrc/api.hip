@@ -1,0 +1,149 @@
+// api.hip -- the extern "C" entry points of libpkv (declared in include/pkv.h).
+// Host-side validation of scalar arguments, then kernel launches on the
+// caller's stream.  Nothing here reads device memory or allocates.
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
+                              const int32_t* num_computed_tokens, const int32_t* block_table,
+                              int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens,
+                              int32_t qsl_len, int32_t block_size, int64_t num_blocks,
+                              int32_t* req_indices, int32_t* positions, int64_t* slot_mapping,
+                              int32_t* query_start_loc, int32_t* seq_lens,
+                              int32_t* logits_indices, void* stream) {
+  if (num_reqs < 0 || num_tokens < 0 || qsl_len < num_reqs + 1 || block_size < 1 ||
+      num_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!query_start_loc) return PKV_ERR_INVALID_ARG;
+  if (num_reqs > 0 &&
+      (!num_scheduled_tokens || !num_computed_tokens || !seq_lens || !logits_indices))
+    return PKV_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (num_reqs == 0 || !block_table || bt_row_stride < 1 || !req_indices ||
+                         !positions || !slot_mapping))
+    return PKV_ERR_INVALID_ARG;
+  return launch_status(pkv::launch_prepare(
+      num_scheduled_tokens, num_computed_tokens, block_table, bt_row_stride, num_reqs,
+      num_tokens, qsl_len, block_size, num_blocks, req_indices, positions, slot_mapping,
+      query_start_loc, seq_lens, logits_indices, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_kv_cache_write(const void* key, const void* value, int64_t key_row_stride,
+                              int64_t value_row_stride, void* key_cache, void* value_cache,
+                              int64_t num_blocks, const int64_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, pkv_dtype dtype, void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  const int32_t esz = dtype == PKV_BF16 ? 2 : 4;
+  if ((int64_t)head_dim * esz % 16 != 0 || head_dim > 256) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (key_row_stride < row || value_row_stride < row) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      key_row_stride * esz % 16 != 0 || value_row_stride * esz % 16 != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_kv_write(key, value, key_row_stride, value_row_stride,
+                                            key_cache, value_cache, num_blocks, slot_mapping,
+                                            num_tokens, num_kv_heads, head_dim, block_size, esz,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_query_len,
+                                           int32_t max_seq_len, int32_t split_tokens,
+                                           pkv_dtype dtype) {
+  pkv::AttnPlan plan;
+  if (!pkv::make_attn_plan(num_reqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                           max_query_len, max_seq_len, split_tokens, dtype, &plan))
+    return 0;
+  return plan.total_bytes;
+}
+
+pkv_status pkv_paged_attention_varlen(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, int32_t split_tokens, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (num_reqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0 ||
+      num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      split_tokens < 0 || split_tokens % 32 != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (block_size != pkv::kBlock) return PKV_ERR_UNSUPPORTED;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (dtype == PKV_BF16 && group > pkv::kPairsPerTile) return PKV_ERR_UNSUPPORTED;
+  if (num_q_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  pkv::AttnPlan plan;
+  if (!pkv::make_attn_plan(num_reqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                           max_query_len, max_seq_len, split_tokens, dtype, &plan))
+    return PKV_ERR_INVALID_ARG;
+  if (plan.max_items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
+  if (!q || !key_cache || !value_cache || !out || !query_start_loc || !seq_lens || !block_table)
+    return PKV_ERR_INVALID_ARG;
+  const int64_t row = (int64_t)num_q_heads * head_dim;
+  const int32_t esz = dtype == PKV_BF16 ? 2 : 4;
+  if (q_row_stride < row || out_row_stride < row || bt_row_stride < 1 || num_blocks < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      q_row_stride * esz % 16 != 0 || out_row_stride * esz % 16 != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (plan.total_bytes > 0 &&
+      (workspace == nullptr || workspace_bytes < plan.total_bytes ||
+       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+    return PKV_ERR_WORKSPACE;
+
+  pkv::AttnArgs a;
+  a.q = q;
+  a.q_stride = q_row_stride;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.num_blocks = num_blocks;
+  a.out = out;
+  a.out_stride = out_row_stride;
+  a.qsl = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.bt_stride = bt_row_stride;
+  a.num_reqs = num_reqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PKV_BF16) return launch_status(pkv::launch_attention_bf16(a, plan, workspace, s));
+  return launch_status(pkv::launch_attention_f32(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,797 @@
+// attention.hip -- paged, variable-length causal attention for gfx950.
+//
+// What is computed ("How vLLM Works Internally: A Deep Dive", "How the Kernel
+// Works"): for every query row, look up its request's block table, fetch K
+// from scattered physical blocks, score, softmax, and sum V with those
+// weights.  A query at in-chunk offset t of a request with q_len new tokens
+// and seq_len total tokens is at position seq_len - q_len + t and sees keys
+// 0..that position.  Long decode contexts are split into partitions whose
+// partial softmax results a second pass combines ("PagedAttention V2").
+//
+// bf16 path (three launches per call, all on the caller's stream):
+//  1. plan:   one workgroup turns query_start_loc / seq_lens into a work list
+//             in the workspace: prefill tiles first (latest rows first, since
+//             they see the most keys), then decode items.  Host code never
+//             reads device data, so the list is built on the device.
+//  2. main:   one workgroup (4 waves) per work item; prompt-chunk tiles and
+//             single-token decodes of the same step run in this one launch.
+//             * decode item = (request, kv head, partition): the q heads of
+//               the kv head (and, for short multi-token queries, their rows)
+//               form the 16-wide N side of v_mfma_f32_16x16x32_bf16; the 4
+//               waves split the partition's 32-token steps and merge their
+//               (max, sum, acc) states through LDS at the end.
+//             * prefill item = (request, kv head, 256 (row, head) pairs): each
+//               wave owns 64 pairs (4 MFMA N tiles) and walks every key step
+//               its rows can see.
+//             Both walk the context two 16-token blocks at a time: K rows are
+//             the MFMA A operand (16 tokens x 32 dims per load); S^T = K Q^T
+//             lands with 4 tokens of one column per lane, which is exactly
+//             the B-operand layout of P^T in O^T = V^T P^T, so the softmax
+//             probabilities feed the second MFMA without leaving registers.
+//             V blocks are stored dim-major, so V^T rows are contiguous runs
+//             of 4 tokens (8 bytes) per lane.  Online softmax: running max by
+//             two cross-lane shuffles, per-lane partial sums reduced once.
+//  3. reduce: combines partition partials of split decode items.
+// fp32 path: one wave per (row, q head), fp32 vector math, no partitions.
+#include <math.h>
+
+#include <algorithm>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = kWaves * 64;
+
+__device__ inline bf16x8 ld_b128(const char* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ inline u32x2 ld_b64(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline unsigned short bf16_bits(float x) {
+  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
+}
+
+// Keep element k of a 4 x bf16 run iff bit k of `keep` is set.
+__device__ inline u32x2 keep_bf16x4(u32x2 v, unsigned keep) {
+  v.x &= ((keep & 1u) ? 0x0000FFFFu : 0u) | ((keep & 2u) ? 0xFFFF0000u : 0u);
+  v.y &= ((keep & 4u) ? 0x0000FFFFu : 0u) | ((keep & 8u) ? 0xFFFF0000u : 0u);
+  return v;
+}
+
+__device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Rows of request r, or 0 when its query_start_loc range leaves [0, num_tokens)
+// (a broken precondition): such a request gets no work, so no kernel touches
+// rows outside q / out.
+__device__ inline int valid_q_len(const int32_t* qsl, int r, int num_tokens) {
+  const int q0 = qsl[r], q1 = qsl[r + 1];
+  return (q0 >= 0 && q1 <= num_tokens && q1 >= q0) ? q1 - q0 : 0;
+}
+
+// Partitions of one decode context; identical in plan, main and reduce.
+__device__ inline int num_splits(int seq_len, int split_tokens, int max_splits) {
+  return min(max_splits, max(1, ceil_div(max(seq_len, 1), split_tokens)));
+}
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+__device__ inline int block_scan_1024(int v, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(v, off, 64);
+    if (lane >= off) v += up;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int x = wave_tot[w];
+    before += (w < wave) ? x : 0;
+    sum += x;
+  }
+  __syncthreads();
+  *total = sum;
+  return v + before;
+}
+
+__global__ __launch_bounds__(1024) void attn_plan_kernel(
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t num_reqs,
+    int32_t num_tokens, int32_t num_kv_heads, int32_t group, int32_t split_tokens, int32_t max_splits,
+    int64_t max_items, int4* __restrict__ items, int32_t* __restrict__ n_items) {
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x;
+  int64_t carry = 0;  // work items emitted so far (in units of kv-head groups)
+  // pass 1: prefill tiles, pass 2: decode items
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int base = 0; base < num_reqs; base += 1024) {
+      const int r = base + tid;
+      int cnt = 0, nsplit = 0;
+      if (r < num_reqs) {
+        const int q_len = valid_q_len(qsl, r, num_tokens);
+        const int pairs = q_len * group;
+        if (pass == 0 && pairs > kPairsPerTile) cnt = ceil_div(pairs, kPrefillPairs);
+        if (pass == 1 && pairs >= 1 && pairs <= kPairsPerTile) {
+          nsplit = num_splits(seq_lens[r], split_tokens, max_splits);
+          cnt = nsplit;
+        }
+      }
+      int total;
+      const int incl = block_scan_1024(cnt, s_wave, &total);
+      const int64_t first = carry + incl - cnt;
+      for (int k = 0; k < cnt; ++k) {
+        for (int h = 0; h < num_kv_heads; ++h) {
+          const int64_t idx = (first + k) * num_kv_heads + h;
+          if (idx >= max_items) break;
+          // prefill: latest tile first; decode: partition k of nsplit
+          items[idx] = pass == 0 ? make_int4(r, h, cnt - 1 - k, -1) : make_int4(r, h, k, nsplit);
+        }
+      }
+      carry += total;
+    }
+  }
+  if (tid == 0) {
+    const int64_t n = carry * num_kv_heads;
+    *n_items = (int32_t)(n < max_items ? n : max_items);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// main: shared step of the decode and prefill items
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct Geometry {
+  static constexpr int KS = D / 32;                   // QK k-steps of 32 dims
+  static constexpr int DT = D / 16;                   // PV output dim tiles
+  static constexpr int64_t kHeadBytes = kBlock * D * 2;  // one (block, kv head) run
+};
+
+// Loads of one 32-token step: K rows of blocks j0 and j1 (A operand of S^T),
+// and 4-token V^T runs of both blocks for every 16-dim tile.
+template <int D>
+struct StepLoads {
+  bf16x8 k0[Geometry<D>::KS], k1[Geometry<D>::KS];
+  u32x2 v0[Geometry<D>::DT], v1[Geometry<D>::DT];
+};
+
+template <int D>
+__device__ inline void issue_step_loads(StepLoads<D>& ld, const char* kb0, const char* kb1,
+                                        const char* vb0, const char* vb1, int k_lane,
+                                        int v_lane) {
+#pragma unroll
+  for (int s = 0; s < Geometry<D>::KS; ++s) {
+    ld.k0[s] = ld_b128(kb0 + k_lane + s * 64);
+    ld.k1[s] = ld_b128(kb1 + k_lane + s * 64);
+  }
+#pragma unroll
+  for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
+    ld.v0[dt] = ld_b64(vb0 + v_lane + dt * (16 * kBlock * 2));
+    ld.v1[dt] = ld_b64(vb1 + v_lane + dt * (16 * kBlock * 2));
+  }
+}
+
+// Online-softmax state of one 16-column tile held by a wave.
+template <int D>
+struct TileState {
+  f32x4 o[Geometry<D>::DT];  // O^T: lane (n, g) holds dims 16*dt + 4*g + i of column n
+  float m;                   // running max of raw scores (same in all lanes of a column)
+  float l;                   // this lane's partial sum of exp weights
+};
+
+template <int D>
+__device__ inline void tile_init(TileState<D>& st) {
+#pragma unroll
+  for (int dt = 0; dt < Geometry<D>::DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// One 32-token step for one column tile: S^T = K Q^T, mask, online softmax,
+// O^T += V^T P^T.  `kpos` is the position of element 0 of this lane's block-0
+// run (block j0 start + 4 * g); element i of block 1 is at kpos + 16 + i.
+template <int D, bool MASK>
+__device__ inline void tile_step(TileState<D>& st, const bf16x8* qf, const StepLoads<D>& ld,
+                                 const bf16x8* vf, int kpos, int p_col, bool ok0, bool ok1,
+                                 float c2) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < Geometry<D>::KS; ++s) {
+    s0 = mfma_bf16(ld.k0[s], qf[s], s0);
+    s1 = mfma_bf16(ld.k1[s], qf[s], s1);
+  }
+  if (MASK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s0[i] = (ok0 && kpos + i <= p_col) ? s0[i] : -INFINITY;
+      s1[i] = (ok1 && kpos + 16 + i <= p_col) ? s1[i] : -INFINITY;
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                   fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2((st.m - m_use) * c2);
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = fast_exp2((s0[i] - m_use) * c2);
+    p[4 + i] = fast_exp2((s1[i] - m_use) * c2);
+  }
+  st.l = st.l * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+  st.m = m_new;
+  bf16x8 pf;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pf[i] = static_cast<__bf16>(p[i]);
+#pragma unroll
+  for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
+    st.o[dt] *= alpha;
+    st.o[dt] = mfma_bf16(vf[dt], pf, st.o[dt]);
+  }
+}
+
+// V^T operand of one step: elements 0..3 = block j0 tokens 4g..4g+3, 4..7 =
+// block j1 tokens 4g..4g+3.  Under MASK, tokens past the context or in an
+// invalid block are zeroed (their probability is 0, but the pool may hold NaN
+// there and 0 * NaN would poison the sum).
+template <int D, bool MASK>
+__device__ inline void build_v_operand(bf16x8* vf, const StepLoads<D>& ld, int kpos, int seq_len,
+                                       bool ok0, bool ok1) {
+  unsigned keep0 = 0xFu, keep1 = 0xFu;
+  if (MASK) {
+    keep0 = 0u;
+    keep1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      keep0 |= (ok0 && kpos + i < seq_len) ? (1u << i) : 0u;
+      keep1 |= (ok1 && kpos + 16 + i < seq_len) ? (1u << i) : 0u;
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
+    u32x2 a = ld.v0[dt], b = ld.v1[dt];
+    if (MASK) {
+      a = keep_bf16x4(a, keep0);
+      b = keep_bf16x4(b, keep1);
+    }
+    vf[dt] = __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+  }
+}
+
+struct StepBlocks {
+  const char* kb0;
+  const char* kb1;
+  const char* vb0;
+  const char* vb1;
+  bool ok0, ok1;
+};
+
+// Physical blocks of logical blocks j0 = 2*step and j0 + 1 (wave-uniform).
+template <int D>
+__device__ inline StepBlocks step_blocks(const AttnArgs& a, const int32_t* bt, int step, int nblk,
+                                         const char* kbase, const char* vbase) {
+  const int j0 = 2 * step, j1 = j0 + 1;
+  int b0 = (j0 < nblk && j0 < a.bt_stride) ? bt[j0] : -1;
+  int b1 = (j1 < nblk && j1 < a.bt_stride) ? bt[j1] : -1;
+  StepBlocks sb;
+  sb.ok0 = b0 >= 0 && b0 < a.num_blocks;
+  sb.ok1 = b1 >= 0 && b1 < a.num_blocks;
+  const int64_t stride = (int64_t)a.num_kv_heads * Geometry<D>::kHeadBytes;
+  const int64_t o0 = (sb.ok0 ? (int64_t)b0 : 0) * stride;
+  const int64_t o1 = (sb.ok1 ? (int64_t)b1 : 0) * stride;
+  sb.kb0 = kbase + o0;
+  sb.kb1 = kbase + o1;
+  sb.vb0 = vbase + o0;
+  sb.vb1 = vbase + o1;
+  return sb;
+}
+
+// ---------------------------------------------------------------------------
+// decode item
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct DecodeSmem {
+  float m[kWaves][kPairsPerTile];
+  float l[kWaves][kPairsPerTile];
+  float o[kWaves][kPairsPerTile][D + 4];
+};
+
+template <int D>
+__device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kvh, int split,
+                           int nsplit, int max_splits, float* __restrict__ ml,
+                           float* __restrict__ opart, DecodeSmem<D>& sm) {
+  using Geo = Geometry<D>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int row0 = a.qsl[r];
+  const int q_len = a.qsl[r + 1] - row0;
+  const int L = a.seq_lens[r];
+  const int pairs = q_len * group;
+
+  // MFMA column n = (row t, head hh) pair n of this item
+  const bool col_ok = n < pairs;
+  const int t = col_ok ? n / group : 0;
+  const int head = kvh * group + (col_ok ? n - t * group : 0);
+  const int p_col = col_ok ? L - q_len + t : -1;
+  const int p_min = L - q_len;
+
+  bf16x8 qf[Geo::KS];
+  {
+    const char* qrow = static_cast<const char*>(a.q) +
+                       ((int64_t)(row0 + t) * a.q_stride + (int64_t)head * D) * 2;
+#pragma unroll
+    for (int s = 0; s < Geo::KS; ++s) {
+      qf[s] = col_ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
+                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  const int nblk = L > 0 ? ceil_div(L, kBlock) : 0;
+  const int steps_all = ceil_div(nblk, 2);
+  const int per_split = ceil_div(steps_all, nsplit);
+  const int sp_begin = split * per_split;
+  const int sp_end = min(steps_all, sp_begin + per_split);
+  const int per_wave = ceil_div(max(0, sp_end - sp_begin), kWaves);
+  const int w_begin = sp_begin + wave * per_wave;
+  const int w_end = min(sp_end, w_begin + per_wave);
+
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
+  const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
+  const int k_lane = (n * D + 8 * g) * 2;
+  const int v_lane = (n * kBlock + 4 * g) * 2;
+
+  TileState<D> st;
+  tile_init(st);
+  if (w_begin < w_end) {
+    StepBlocks sb = step_blocks<D>(a, bt, w_begin, nblk, kbase, vbase);
+    StepLoads<D> cur;
+    issue_step_loads<D>(cur, sb.kb0, sb.kb1, sb.vb0, sb.vb1, k_lane, v_lane);
+    for (int step = w_begin; step < w_end; ++step) {
+      // prefetch the next step before computing this one
+      StepBlocks nb = sb;
+      StepLoads<D> nxt;
+      const bool more = step + 1 < w_end;
+      if (more) {
+        nb = step_blocks<D>(a, bt, step + 1, nblk, kbase, vbase);
+        issue_step_loads<D>(nxt, nb.kb0, nb.kb1, nb.vb0, nb.vb1, k_lane, v_lane);
+      }
+      const int kpos = step * 2 * kBlock + 4 * g;
+      const bool mask = (step * 2 * kBlock + 2 * kBlock - 1 > p_min) || !sb.ok0 || !sb.ok1;
+      bf16x8 vf[Geo::DT];
+      if (mask) {
+        build_v_operand<D, true>(vf, cur, kpos, L, sb.ok0, sb.ok1);
+        tile_step<D, true>(st, qf, cur, vf, kpos, p_col, sb.ok0, sb.ok1, c2);
+      } else {
+        build_v_operand<D, false>(vf, cur, kpos, L, true, true);
+        tile_step<D, false>(st, qf, cur, vf, kpos, p_col, true, true, c2);
+      }
+      if (more) {
+        cur = nxt;
+        sb = nb;
+      }
+    }
+  }
+
+  // merge the four waves' states
+  float l_tot = st.l + __shfl_xor(st.l, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (g == 0) {
+    sm.m[wave][n] = st.m;
+    sm.l[wave][n] = l_tot;
+  }
+#pragma unroll
+  for (int dt = 0; dt < Geo::DT; ++dt)
+    *reinterpret_cast<f32x4*>(&sm.o[wave][n][16 * dt + 4 * g]) = st.o[dt];
+  __syncthreads();
+
+  constexpr int kDimsPerThread = D / 16;  // 256 threads = 16 columns x 16 dim chunks
+  const int cn = threadIdx.x >> 4;
+  const int cd = (threadIdx.x & 15) * kDimsPerThread;
+  if (cn < pairs) {
+    float mw[kWaves];
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = sm.m[w][cn];
+      mmax = fmaxf(mmax, mw[w]);
+    }
+    float lsum = 0.f;
+    float acc[kDimsPerThread];
+#pragma unroll
+    for (int k = 0; k < kDimsPerThread; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = (mw[w] == -INFINITY) ? 0.f : fast_exp2((mw[w] - mmax) * c2);
+      lsum += f * sm.l[w][cn];
+#pragma unroll
+      for (int k = 0; k < kDimsPerThread; ++k) acc[k] += f * sm.o[w][cn][cd + k];
+    }
+    const int tt = cn / group;
+    const int hh = kvh * group + (cn - tt * group);
+    if (nsplit == 1) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      unsigned short bits[kDimsPerThread];
+#pragma unroll
+      for (int k = 0; k < kDimsPerThread; ++k) bits[k] = bf16_bits(acc[k] * inv);
+      char* dst = static_cast<char*>(a.out) +
+                  ((int64_t)(row0 + tt) * a.out_stride + (int64_t)hh * D + cd) * 2;
+      if (kDimsPerThread == 8) {
+        u32x4 v;
+        __builtin_memcpy(&v, bits, 16);
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        u32x2 v;
+        __builtin_memcpy(&v, bits, 8);
+        *reinterpret_cast<u32x2*>(dst) = v;
+      }
+    } else {
+      const int64_t idx =
+          (((int64_t)r * a.num_kv_heads + kvh) * max_splits + split) * kPairsPerTile + cn;
+      if ((threadIdx.x & 15) == 0) {
+        ml[2 * idx] = mmax;
+        ml[2 * idx + 1] = lsum;
+      }
+      float* dst = opart + idx * D + cd;
+#pragma unroll
+      for (int k = 0; k < kDimsPerThread; k += 4)
+        *reinterpret_cast<f32x4*>(dst + k) = f32x4{acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill item
+// ---------------------------------------------------------------------------
+
+template <int D>
+__device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int kvh, int mtile) {
+  using Geo = Geometry<D>;
+  constexpr int NT = kPrefillTilesPerWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int row0 = a.qsl[r];
+  const int q_len = a.qsl[r + 1] - row0;
+  const int L = a.seq_lens[r];
+  const int pairs = q_len * group;
+  const int pbase = mtile * kPrefillPairs + wave * (NT * kPairsPerTile);
+  if (pbase >= pairs) return;  // this wave has no rows (no barrier follows)
+
+  bf16x8 qf[NT][Geo::KS];
+  int p_col[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int P = pbase + nt * kPairsPerTile + n;
+    const bool ok = P < pairs;
+    const int t = ok ? P / group : 0;
+    const int head = kvh * group + (ok ? P - t * group : 0);
+    p_col[nt] = ok ? L - q_len + t : -1;
+    const char* qrow = static_cast<const char*>(a.q) +
+                       ((int64_t)(row0 + t) * a.q_stride + (int64_t)head * D) * 2;
+#pragma unroll
+    for (int s = 0; s < Geo::KS; ++s) {
+      qf[nt][s] = ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
+                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  const int t_lo = pbase / group;
+  const int t_hi = (min(pairs, pbase + NT * kPairsPerTile) - 1) / group;
+  const int p_lo = L - q_len + t_lo;
+  const int p_hi = L - q_len + t_hi;
+  const int nblk = L > 0 ? ceil_div(L, kBlock) : 0;
+  const int nsteps = p_hi >= 0 ? min(ceil_div(nblk, 2), p_hi / (2 * kBlock) + 1) : 0;
+
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
+  const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
+  const int k_lane = (n * D + 8 * g) * 2;
+  const int v_lane = (n * kBlock + 4 * g) * 2;
+
+  TileState<D> st[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) tile_init(st[nt]);
+
+  for (int step = 0; step < nsteps; ++step) {
+    const StepBlocks sb = step_blocks<D>(a, bt, step, nblk, kbase, vbase);
+    StepLoads<D> ld;
+    issue_step_loads<D>(ld, sb.kb0, sb.kb1, sb.vb0, sb.vb1, k_lane, v_lane);
+    const int kpos = step * 2 * kBlock + 4 * g;
+    const bool mask = (step * 2 * kBlock + 2 * kBlock - 1 > p_lo) || !sb.ok0 || !sb.ok1;
+    bf16x8 vf[Geo::DT];
+    if (mask) {
+      build_v_operand<D, true>(vf, ld, kpos, L, sb.ok0, sb.ok1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        tile_step<D, true>(st[nt], qf[nt], ld, vf, kpos, p_col[nt], sb.ok0, sb.ok1, c2);
+    } else {
+      build_v_operand<D, false>(vf, ld, kpos, L, true, true);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        tile_step<D, false>(st[nt], qf[nt], ld, vf, kpos, p_col[nt], true, true, c2);
+    }
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float l_tot = st[nt].l + __shfl_xor(st[nt].l, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int P = pbase + nt * kPairsPerTile + n;
+    if (P < pairs) {
+      const int t = P / group;
+      const int head = kvh * group + (P - t * group);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      char* dst = static_cast<char*>(a.out) +
+                  ((int64_t)(row0 + t) * a.out_stride + (int64_t)head * D + 4 * g) * 2;
+#pragma unroll
+      for (int dt = 0; dt < Geo::DT; ++dt) {
+        const f32x4 o = st[nt].o[dt];
+        u16x4 b = {bf16_bits(o[0] * inv), bf16_bits(o[1] * inv), bf16_bits(o[2] * inv),
+                   bf16_bits(o[3] * inv)};
+        *reinterpret_cast<u16x4*>(dst + dt * 32) = b;
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void attn_main_kernel(
+    AttnArgs a, int32_t group, float c2, const int4* __restrict__ items,
+    const int32_t* __restrict__ n_items, int32_t max_splits, float* __restrict__ ml,
+    float* __restrict__ opart) {
+  __shared__ DecodeSmem<D> sm;
+  if ((int)blockIdx.x >= *n_items) return;
+  const int4 it = items[blockIdx.x];
+  if (it.w < 0)
+    run_prefill<D>(a, group, c2, it.x, it.y, it.z);
+  else
+    run_decode<D>(a, group, c2, it.x, it.y, it.z, it.w, max_splits, ml, opart, sm);
+}
+
+// ---------------------------------------------------------------------------
+// reduce: combine the partitions of split decode items
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a, int32_t group, float c2,
+                                                          int32_t split_tokens, int32_t max_splits,
+                                                          const float* __restrict__ ml,
+                                                          const float* __restrict__ opart) {
+  const int r = blockIdx.x / a.num_kv_heads;
+  const int kvh = blockIdx.x - r * a.num_kv_heads;
+  const int row0 = a.qsl[r];
+  const int q_len = valid_q_len(a.qsl, r, a.num_tokens);
+  const int pairs = q_len * group;
+  if (pairs < 1 || pairs > kPairsPerTile) return;
+  const int nsplit = num_splits(a.seq_lens[r], split_tokens, max_splits);
+  if (nsplit <= 1) return;
+  constexpr int kDimsPerThread = D / 16;
+  const int cn = threadIdx.x >> 4;
+  const int cd = (threadIdx.x & 15) * kDimsPerThread;
+  if (cn >= pairs) return;
+  const int64_t base = (((int64_t)r * a.num_kv_heads + kvh) * max_splits) * kPairsPerTile + cn;
+  float mmax = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mmax = fmaxf(mmax, ml[2 * (base + s * kPairsPerTile)]);
+  float lsum = 0.f;
+  float acc[kDimsPerThread];
+#pragma unroll
+  for (int k = 0; k < kDimsPerThread; ++k) acc[k] = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t idx = base + s * kPairsPerTile;
+    const float ms = ml[2 * idx];
+    const float f = (ms == -INFINITY) ? 0.f : fast_exp2((ms - mmax) * c2);
+    lsum += f * ml[2 * idx + 1];
+    const float* src = opart + idx * D + cd;
+#pragma unroll
+    for (int k = 0; k < kDimsPerThread; k += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + k);
+      acc[k] += f * v[0];
+      acc[k + 1] += f * v[1];
+      acc[k + 2] += f * v[2];
+      acc[k + 3] += f * v[3];
+    }
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int tt = cn / group;
+  const int hh = kvh * group + (cn - tt * group);
+  unsigned short bits[kDimsPerThread];
+#pragma unroll
+  for (int k = 0; k < kDimsPerThread; ++k) bits[k] = bf16_bits(acc[k] * inv);
+  char* dst = static_cast<char*>(a.out) +
+              ((int64_t)(row0 + tt) * a.out_stride + (int64_t)hh * D + cd) * 2;
+  if (kDimsPerThread == 8) {
+    u32x4 v;
+    __builtin_memcpy(&v, bits, 16);
+    *reinterpret_cast<u32x4*>(dst) = v;
+  } else {
+    u32x2 v;
+    __builtin_memcpy(&v, bits, 8);
+    *reinterpret_cast<u32x2*>(dst) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one wave per (row, q head)
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int32_t group) {
+  constexpr int PER = D / 64;
+  const int row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int R = a.num_reqs;
+  int lo = 0, hi = R - 1;  // last request whose first row is <= row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.qsl[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo;
+  const int row0 = a.qsl[r];
+  const int q_len = a.qsl[r + 1] - row0;
+  float* out = static_cast<float*>(a.out) + (int64_t)row * a.out_stride + (int64_t)h * D;
+  if (row < row0 || row >= row0 + q_len) {  // inconsistent query_start_loc
+#pragma unroll
+    for (int k = 0; k < PER; ++k) out[lane + 64 * k] = 0.f;
+    return;
+  }
+  const int L = a.seq_lens[r];
+  const int p = L - q_len + (row - row0);
+  const int kvh = h / group;
+  const float* qrow = static_cast<const float*>(a.q) + (int64_t)row * a.q_stride + (int64_t)h * D;
+  float qv[PER], o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    qv[k] = qrow[lane + 64 * k];
+    o[k] = 0.f;
+  }
+  const float* kc = static_cast<const float*>(a.key_cache);
+  const float* vc = static_cast<const float*>(a.value_cache);
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j <= p; ++j) {
+    const int lb = j / kBlock;
+    if (lb >= a.bt_stride) break;
+    const int32_t phys = bt[lb];
+    if (phys < 0 || phys >= a.num_blocks) continue;
+    const int off = j - lb * kBlock;
+    const int64_t head_base = (int64_t)phys * a.num_kv_heads + kvh;
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) dot += qv[k] * kc[(head_base * kBlock + off) * D + lane + 64 * k];
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh, 64);
+    const float s = dot * a.scale;
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new);
+    const float pj = expf(s - m_new);
+    l = l * alpha + pj;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      o[k] = o[k] * alpha + pj * vc[(head_base * D + lane + 64 * k) * kBlock + off];
+    m = m_new;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) out[lane + 64 * k] = o[k] * inv;
+}
+
+template <int D>
+hipError_t launch_bf16_d(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                         hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int32_t* n_items = reinterpret_cast<int32_t*>(ws);
+  int4* items = reinterpret_cast<int4*>(ws + plan.items_offset);
+  float* ml = plan.max_splits > 1 ? reinterpret_cast<float*>(ws + plan.ml_offset) : nullptr;
+  float* opart = plan.max_splits > 1 ? reinterpret_cast<float*>(ws + plan.o_offset) : nullptr;
+  const float c2 = a.scale * kLog2e;
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.seq_lens,
+                     a.num_reqs, a.num_tokens, a.num_kv_heads, plan.group, plan.split_tokens, plan.max_splits,
+                     plan.max_items, items, n_items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (plan.max_items > 0) {
+    hipLaunchKernelGGL(attn_main_kernel<D>, dim3((unsigned)plan.max_items), dim3(kThreads), 0,
+                       stream, a, plan.group, c2, items, n_items, plan.max_splits, ml, opart);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (plan.max_splits > 1) {
+    hipLaunchKernelGGL(attn_reduce_kernel<D>, dim3(a.num_reqs * a.num_kv_heads), dim3(256), 0,
+                       stream, a, plan.group, c2, plan.split_tokens, plan.max_splits, ml, opart);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                    int32_t max_seq_len, int32_t split_tokens, pkv_dtype dtype, AttnPlan* plan) {
+  if (num_reqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_query_len < 0 ||
+      max_seq_len < 0 || split_tokens < 0 || split_tokens % 32 != 0)
+    return false;
+  AttnPlan p = {};
+  p.group = num_q_heads / num_kv_heads;
+  if (dtype != PKV_BF16) {
+    *plan = p;
+    return true;
+  }
+  const int64_t pairs_per_req = (int64_t)num_reqs * num_kv_heads;
+  int32_t st = split_tokens;
+  if (st == 0) {
+    // Partition long decode contexts only when the batch alone cannot fill
+    // the chip: aim for ~2048 workgroups of at least 256 tokens each.
+    const int64_t want = 2048;
+    if (pairs_per_req >= want || max_seq_len <= 256) {
+      st = ((std::max(max_seq_len, 1) + 31) / 32) * 32;
+    } else {
+      const int64_t per = ((int64_t)max_seq_len * pairs_per_req + want - 1) / want;
+      st = (int32_t)std::max<int64_t>(256, ((per + 31) / 32) * 32);
+    }
+  }
+  p.split_tokens = st;
+  p.max_splits = std::max(1, (std::max(max_seq_len, 1) + st - 1) / st);
+  const int64_t g = p.group;
+  const int64_t prefill_tiles = ((int64_t)num_tokens * g + kPrefillPairs - 1) / kPrefillPairs +
+                                num_reqs;
+  p.max_items = (int64_t)num_kv_heads * ((int64_t)num_reqs * p.max_splits + prefill_tiles);
+  if (num_tokens == 0) p.max_items = 0;
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 256;  // header: item count
+  p.items_offset = off;
+  off = align(off + (size_t)p.max_items * sizeof(int4));
+  if (p.max_splits > 1) {
+    const size_t slots = (size_t)pairs_per_req * p.max_splits * kPairsPerTile;
+    p.ml_offset = off;
+    off = align(off + slots * 2 * sizeof(float));
+    p.o_offset = off;
+    off = align(off + slots * (size_t)head_dim * sizeof(float));
+  }
+  p.total_bytes = off;
+  *plan = p;
+  return true;
+}
+
+hipError_t launch_attention_bf16(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                                 hipStream_t stream) {
+  if (a.num_tokens == 0 || a.num_reqs == 0) return hipSuccess;
+  if (a.head_dim == 128) return launch_bf16_d<128>(a, plan, workspace, stream);
+  return launch_bf16_d<64>(a, plan, workspace, stream);
+}
+
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {
+  if (a.num_tokens == 0 || a.num_reqs == 0) return hipSuccess;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  dim3 grid(a.num_tokens, a.num_q_heads);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, a, group);
+  else
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, a, group);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

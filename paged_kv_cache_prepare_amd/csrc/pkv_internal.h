@@ -1,0 +1,71 @@
+// pkv_internal.h -- declarations shared by the libpkv HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Attention path constants.
+constexpr int kBlock = 16;          // tokens per KV block the attention kernels read
+constexpr int kPairsPerTile = 16;   // MFMA N width: (query row, q head) pairs per tile
+constexpr int kWaves = 4;           // waves per attention workgroup
+constexpr int kPrefillTilesPerWave = 4;  // 16-pair tiles one wave owns in a prefill item
+constexpr int kPrefillPairs = kWaves * kPrefillTilesPerWave * kPairsPerTile;  // 256
+
+// Host-side plan of one attention call (derived from host scalars only).
+struct AttnPlan {
+  int32_t group;          // q heads per kv head
+  int32_t split_tokens;   // partition size of a decode context (multiple of 32)
+  int32_t max_splits;     // partitions per decode context, upper bound
+  int64_t max_items;      // upper bound on work items (grid size of the main kernel)
+  size_t items_offset;    // byte offsets inside the workspace
+  size_t ml_offset;
+  size_t o_offset;
+  size_t total_bytes;
+};
+
+bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                    int32_t max_seq_len, int32_t split_tokens, pkv_dtype dtype, AttnPlan* plan);
+
+hipError_t launch_prepare(const int32_t* nst, const int32_t* nct, const int32_t* block_table,
+                          int64_t bt_stride, int32_t num_reqs, int32_t num_tokens,
+                          int32_t qsl_len, int32_t block_size, int64_t num_blocks,
+                          int32_t* req_indices, int32_t* positions, int64_t* slot_mapping,
+                          int32_t* qsl, int32_t* seq_lens, int32_t* logits_indices,
+                          hipStream_t stream);
+
+hipError_t launch_kv_write(const void* key, const void* value, int64_t key_stride,
+                           int64_t value_stride, void* key_cache, void* value_cache,
+                           int64_t num_blocks, const int64_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t elem_bytes, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  int64_t q_stride;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t num_blocks;
+  void* out;
+  int64_t out_stride;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int32_t num_reqs;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float scale;
+};
+
+hipError_t launch_attention_bf16(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                                 hipStream_t stream);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,170 @@
+"""GPU parity of pkv_paged_attention_varlen against the fp64 oracle, through
+the C ABI: the five named configurations at full size (sampled rows, in the
+launch configuration the benchmark times), and small cases that span several
+tiles with ragged tails, every GQA group size, both head sizes and dtypes,
+forced context partitions, NaN-poisoned pools and bad block ids."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_prepare_amd as pkv
+from paged_kv_cache_prepare_amd import workloads
+
+from gpu_helpers import (assert_attention_close, assert_prepare_equal, bits_view, device,
+                         gpu_step, log, oracle_step)
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(wl, n_per_request=3, max_rows=48, seed=0):
+    """First, last and a random row of requests, capped; all rows when few."""
+    T = wl.num_tokens
+    if T <= max_rows:
+        return None
+    rng = np.random.default_rng(seed)
+    qsl = np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)])
+    rows = set()
+    reqs = np.nonzero(wl.num_scheduled_tokens)[0]
+    # every prefill request gets a spread of rows; decodes are sampled
+    for r in reqs:
+        n = int(wl.num_scheduled_tokens[r])
+        if n > 1:
+            rows.update(int(x) for x in np.linspace(qsl[r], qsl[r + 1] - 1, 12).astype(int))
+    dec = [r for r in reqs if wl.num_scheduled_tokens[r] == 1]
+    for r in rng.permutation(dec)[:max_rows - len(rows)]:
+        rows.add(int(qsl[r]))
+    return np.array(sorted(rows), np.int32)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_attention_config(idx):
+    log(f"config {idx}: {workloads.CONFIG_NAMES[idx]}")
+    wl = workloads.config(idx, device=device())
+    prep, kc, vc, out = gpu_step(wl)
+    rows = sample_rows(wl)
+    ref_prep, okc, ovc, ref = oracle_step(wl, rows=rows)
+    assert_prepare_equal(prep, ref_prep, f"config {idx}")
+    assert torch.equal(bits_view(kc.cpu()), bits_view(okc)), "K pool"
+    assert torch.equal(bits_view(vc.cpu()), bits_view(ovc)), "V pool"
+    got = out if rows is None else out[torch.from_numpy(rows).long().to(out.device)]
+    assert_attention_close(got, ref, wl.dtype, f"config {idx} ({'all' if rows is None else len(rows)} rows)")
+
+
+# (nst, nct, Hq, Hkv, d) -- decode items, multi-row decode items (q_len * G <= 16),
+# prefill tiles with ragged tails, chunks that start mid-sequence, empty requests.
+SMALL = [
+    ([1, 1, 1, 1], [0, 15, 16, 300], 4, 4, 128),
+    ([1] * 9, [5, 31, 32, 33, 63, 64, 100, 511, 1000], 32, 8, 128),
+    ([2, 4, 1, 3], [17, 40, 0, 2], 8, 2, 128),             # 2*4, 4*4... multi-row decodes (G=4)
+    ([16, 5], [3, 70], 1, 1, 128),                          # G=1, 16 rows still one decode item
+    ([300, 1, 0, 47], [0, 90, 12, 200], 8, 2, 128),        # prefill tiles + ragged tail
+    ([700], [1234], 32, 8, 128),                            # long chunk mid-sequence
+    ([65, 1, 129], [0, 33, 500], 16, 1, 128),               # G=16 (MQA-like)
+    ([1, 1, 40], [7, 200, 9], 4, 2, 64),                    # head_dim 64
+    ([3, 1], [0, 77], 2, 2, 64),
+    ([0, 0, 5, 0], [0, 4, 60, 3], 6, 3, 128),               # G=2 with empty requests
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_attention_small(case, dtype):
+    nst, nct, Hq, Hkv, d = SMALL[case]
+    wl = workloads.build(f"small{case}", nst, nct, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                         dtype=dtype, seed=50 + case, device=device(), pool_slack=1.3,
+                         extra_table_cols=2)
+    prep, kc, vc, out = gpu_step(wl)
+    _, _, _, ref = oracle_step(wl)
+    assert_attention_close(out, ref, dtype, f"small{case} {dtype}")
+
+
+@pytest.mark.parametrize("split_tokens", [32, 64, 96, 256])
+def test_attention_forced_partitions(split_tokens):
+    """Split-KV (two-pass) results agree with the oracle and with one pass."""
+    nst = [1, 1, 1, 2, 1]
+    nct = [2000, 31, 700, 901, 129]
+    wl = workloads.build("split", nst, nct, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         seed=77, device=device(), pool_slack=1.1)
+    _, _, _, one = gpu_step(wl, split_tokens=2048 + 32)
+    _, _, _, many = gpu_step(wl, split_tokens=split_tokens)
+    _, _, _, ref = oracle_step(wl)
+    assert_attention_close(one, ref, wl.dtype, "single pass")
+    assert_attention_close(many, ref, wl.dtype, f"split {split_tokens}")
+
+
+def test_attention_block_permutation_invariance():
+    """Moving physical blocks (and rewriting the table) leaves the GPU result
+    bit-identical: the kernel's arithmetic order depends only on logical order."""
+    wl = workloads.build("perm", [1, 40, 1], [300, 20, 1000], num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, seed=5, device=device(), pool_slack=1.5)
+    _, kc, vc, out = gpu_step(wl)
+    perm = torch.randperm(wl.num_blocks, generator=torch.Generator().manual_seed(1))
+    kc2 = torch.empty_like(kc)
+    vc2 = torch.empty_like(vc)
+    pd = perm.to(kc.device)
+    kc2[pd] = kc
+    vc2[pd] = vc
+    bt2 = np.where(wl.block_table >= 0, perm.numpy()[np.maximum(wl.block_table, 0)],
+                   -1).astype(np.int32)
+    qsl = torch.tensor(np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)]),
+                       dtype=torch.int32, device=kc.device)
+    sl = torch.tensor(wl.num_scheduled_tokens + wl.num_computed_tokens, dtype=torch.int32,
+                      device=kc.device)
+    out2 = pkv.paged_attention(wl.q, kc2, vc2, qsl, sl, torch.from_numpy(bt2).to(kc.device),
+                               max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                               scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(bits_view(out), bits_view(out2))
+
+
+def test_attention_bad_block_ids_contribute_nothing():
+    """A table entry outside the pool contributes no keys and nothing is read
+    outside the pool.  For a single-token query every key is visible, so the
+    expected result is attention over the table with that entry removed."""
+    wl = workloads.build("badid", [1, 1], [100, 100], num_q_heads=4, num_kv_heads=2,
+                         head_dim=128, seed=9, device=device())
+    dev = device()
+    bt = wl.block_table.copy()
+    bt[0, 2] = wl.num_blocks + 1000
+    bt[1, 0] = -7
+    qsl = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)
+    # history only (no write this step): positions 0..99 hold values
+    sl = torch.tensor([100, 100], dtype=torch.int32, device=dev)
+    out = pkv.paged_attention(wl.q, wl.key_cache, wl.value_cache, qsl, sl,
+                              torch.from_numpy(bt).to(dev), max_query_len=1, max_seq_len=100,
+                              scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    dropped = np.full_like(bt, -1)
+    dropped[0, :6] = np.delete(wl.block_table[0], 2)[:6]
+    dropped[1, :6] = np.delete(wl.block_table[1], 0)[:6]
+    ref = oracle.attention(wl.q.cpu(), wl.key_cache.cpu(), wl.value_cache.cpu(), [0, 1, 2],
+                           [84, 84], dropped, 16, wl.scale)
+    assert_attention_close(out, ref, wl.dtype, "bad block ids")
+
+
+def test_attention_strided_q_and_out():
+    """q as a view of a fused projection, out written into a wider buffer."""
+    wl = workloads.build("strided", [5, 1, 1], [10, 50, 0], num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, seed=11, device=device())
+    dev = device()
+    T = wl.num_tokens
+    _, kc, vc, ref_out = gpu_step(wl)
+    fused = torch.zeros(T, (8 + 4) * 128, dtype=wl.dtype, device=dev)
+    fused[:, :8 * 128] = wl.q.reshape(T, -1)
+    qv = fused[:, :8 * 128].view(T, 8, 128)
+    big = torch.full((T, 10 * 128), 7.0, dtype=wl.dtype, device=dev)
+    ov = big[:, 128:9 * 128].view(T, 8, 128)
+    qsl = torch.tensor(np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)]),
+                       dtype=torch.int32, device=dev)
+    sl = torch.tensor(wl.num_scheduled_tokens + wl.num_computed_tokens, dtype=torch.int32,
+                      device=dev)
+    pkv.paged_attention(qv, kc, vc, qsl, sl, torch.from_numpy(wl.block_table).to(dev),
+                        max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                        scale=wl.scale, out=ov)
+    torch.cuda.synchronize()
+    assert torch.equal(bits_view(ov.contiguous()), bits_view(ref_out))
+    assert (big[:, :128] == 7).all() and (big[:, 9 * 128:] == 7).all()
