@@ -1,0 +1,238 @@
+"""Benchmark of one step of the paged-attention hot path on one MI355X.
+
+A step is the whole hot path over one batch: prepare_inputs (flat-batch
+indices and slot mapping) -> kv_cache_write (this step's K/V rows into the
+block pool) -> paged_attention_varlen (plan, main, and the split-KV reduce
+when a context is partitioned).  Inputs are resident in HBM before timing;
+outputs, workspace and index buffers are preallocated, so a step allocates
+nothing.
+
+Default workload: the 13B-shaped decode batch (64 requests x 1 token,
+context lengths uniform in [512, 2048], 40 q / 40 kv heads, head_dim 128,
+bf16, 16-token blocks scattered in a pool 1.25x the need).  ``--workload``
+selects another of the five configurations.
+
+Prints one JSON line: tokens/s of the whole step, the roofline of the
+attention call (HBM-bound for decode batches, MFMA-bound for prompt chunks),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--split-tokens", type=int, default=0,
+                   help="context partition size of decode items (0 = library default)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate budget of the CPU oracle baseline")
+    return p.parse_args()
+
+
+def algorithmic_work(wl):
+    """Bytes and flops the attention call must move / compute (one layer)."""
+    nst = wl.num_scheduled_tokens.astype(np.int64)
+    seq = nst + wl.num_computed_tokens.astype(np.int64)
+    e = 2 if str(wl.dtype).endswith("bfloat16") else 4
+    Hq, Hkv, d, bs = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    kv_token_bytes = 2 * Hkv * d * e
+    # unique context tokens: blocks shared by several requests are read once
+    shared = 0
+    if wl.notes.get("shared_blocks"):
+        blocks_logical = int(((seq + bs - 1) // bs).sum())
+        blocks_unique = len(np.unique(wl.block_table[wl.block_table >= 0]))
+        shared = (blocks_logical - blocks_unique) * bs
+    unique_ctx = int(seq.sum()) - shared
+    T = int(nst.sum())
+    q_o_bytes = 2 * T * Hq * d * e
+    table_bytes = int(((seq + bs - 1) // bs).sum()) * 4 + (2 * wl.num_reqs + 1) * 4
+    # visible (query, key) pairs: row t of a request sees seq - q_len + t + 1 keys
+    pairs_dec = pairs_pre = 0
+    for n, L in zip(nst, seq):
+        vis = int(n * (L - n) + n * (n + 1) // 2)
+        if n * (Hq // Hkv) <= 16:
+            pairs_dec += vis
+        else:
+            pairs_pre += vis
+    flops_per_pair = 4 * d * Hq
+    return {
+        "context_tokens": int(seq.sum()),
+        "kv_token_bytes": kv_token_bytes,
+        "bytes_logical": int(seq.sum()) * kv_token_bytes + q_o_bytes + table_bytes,
+        "bytes_unique": unique_ctx * kv_token_bytes + q_o_bytes + table_bytes,
+        "flops_decode": pairs_dec * flops_per_pair,
+        "flops_prefill": pairs_pre * flops_per_pair,
+        "write_bytes": 2 * 2 * T * Hkv * d * e,
+    }
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle timed on host cores on a bounded sample of the same step.
+
+    prepare and the KV write run on the whole batch; attention runs on an
+    evenly strided sample of rows (so prompt-chunk and decode rows appear in
+    the batch's proportions), sized by a short calibration run to take about
+    ``budget_s``.  Rate = sampled rows / (attention time of the sample +
+    prepare and write time prorated to the sample)."""
+    import oracle
+    T = wl.num_tokens
+    kc, vc = wl.key_cache.cpu(), wl.value_cache.cpu()
+    key, val, q = wl.key.cpu(), wl.value.cpu(), wl.q.cpu()
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    prep = oracle.prepare(wl.num_scheduled_tokens, wl.num_computed_tokens, wl.block_table,
+                          wl.block_size, wl.num_blocks)
+    oracle.kv_write(key, val, kc, vc, prep["slot_mapping"], wl.block_size)
+    t_pw = time.perf_counter() - t0
+
+    def attn(rows):
+        t1 = time.perf_counter()
+        oracle.attention(q, kc, vc, prep["query_start_loc"], prep["seq_lens"], wl.block_table,
+                         wl.block_size, wl.scale, rows=rows)
+        return time.perf_counter() - t1
+
+    n = min(T, 2 * threads)
+    rows = np.linspace(0, T - 1, n).astype(np.int32)
+    dt = attn(rows)
+    while n < T and dt < budget_s / 3:
+        n = min(T, max(n + 1, int(n * min(16.0, 0.8 * budget_s / max(dt, 1e-3)))))
+        rows = np.unique(np.linspace(0, T - 1, n).astype(np.int32))
+        n = len(rows)
+        dt = attn(rows)
+    total = dt + t_pw * n / T
+    return {"value": round(n / total, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prepare + kv_write on all {T} rows ({t_pw:.2f} s, prorated), attention "
+                      f"on {n} evenly strided rows of {T} ({dt:.2f} s); fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_prepare_amd as pkv
+    from paged_kv_cache_prepare_amd import workloads
+
+    dev = torch.device("cuda:0")
+    wl = workloads.config(args.workload, device=dev)
+    work = algorithmic_work(wl)
+    T, R = wl.num_tokens, wl.num_reqs
+    nst = torch.from_numpy(wl.num_scheduled_tokens).to(dev)
+    nct = torch.from_numpy(wl.num_computed_tokens).to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    prep = {"req_indices": torch.empty(T, **i32), "positions": torch.empty(T, **i32),
+            "slot_mapping": torch.empty(T, dtype=torch.int64, device=dev),
+            "query_start_loc": torch.empty(R + 1, **i32), "seq_lens": torch.empty(R, **i32),
+            "logits_indices": torch.empty(R, **i32)}
+    kc, vc = wl.key_cache, wl.value_cache
+    out = torch.empty_like(wl.q)
+    ws_bytes = pkv.attention_workspace_bytes(R, T, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                             wl.max_query_len, wl.max_seq_len, args.split_tokens,
+                                             wl.dtype)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.prepare_inputs(nst, nct, bt, num_tokens=T, block_size=wl.block_size,
+                           num_blocks=wl.num_blocks, out=prep)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"],
+                           block_size=wl.block_size)
+        if ev is not None:
+            ev[2].record(stream)
+        pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                            scale=wl.scale, out=out, split_tokens=args.split_tokens,
+                            workspace=ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                   for e in events])
+    t_prep, t_write, t_attn = (float(np.mean(ph[:, i])) for i in range(3))
+
+    attn_s = t_attn / 1e3
+    flops = work["flops_decode"] + work["flops_prefill"]
+    gbs = work["bytes_unique"] / attn_s / 1e9
+    tflops = flops / attn_s / 1e12
+    if work["flops_prefill"] > work["flops_decode"] and \
+            flops / MFMA_BF16_PEAK_TFLOPS / 1e12 > work["bytes_unique"] / HBM_PEAK_GBS / 1e9:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "paged_attention_varlen (plan + attn_main + reduce), HIP events"
+    roof["algorithmic_bytes"] = work["bytes_unique"]
+    roof["algorithmic_flops"] = flops
+    roof["avg_ms"] = round(t_attn, 4)
+
+    cpu = cpu_baseline(wl, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(T / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/Q, random block placement)",
+        "config": {"workload": workloads.CONFIG_NAMES[args.workload], "num_reqs": R,
+                   "num_tokens": T, "context_tokens": work["context_tokens"],
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "seed": wl.seed,
+                   "split_tokens": args.split_tokens},
+        "phases_ms": {"prepare": round(t_prep, 4), "kv_write": round(t_write, 4),
+                      "attention": round(t_attn, 4)},
+        "context_tokens_per_s": round(work["context_tokens"] / (ms_step / 1e3), 1),
+        "attention_hbm_gbs": round(gbs, 1),
+        "attention_tflops": round(tflops, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,7 +54,6 @@ constexpr int kThreads = kWaves * 64;
 __device__ inline bf16x8 ld_b128(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
-__device__ inline u32x2 ld_b64(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -174,19 +173,36 @@ struct StepLoads {
   u32x2 v0[Geometry<D>::DT], v1[Geometry<D>::DT];
 };
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Buffer descriptor word 3 for raw 32-bit buffer accesses on CDNA.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Descriptor of one (block, kv head) run of a pool.  Its record count bounds
+// every access to that 16-token run in hardware; a masked block gets a count
+// of 0, so its loads return zeros without touching memory.
 template <int D>
-__device__ inline void issue_step_loads(StepLoads<D>& ld, const char* kb0, const char* kb1,
-                                        const char* vb0, const char* vb1, int k_lane,
+__device__ inline rsrc_t run_rsrc(const char* run, bool valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(run), 0,
+                                           valid ? (int)Geometry<D>::kHeadBytes : 0, kRsrcWord3);
+}
+
+struct StepRsrc {
+  rsrc_t k0, k1, v0, v1;
+  bool ok0, ok1;
+};
+
+template <int D>
+__device__ inline void issue_step_loads(StepLoads<D>& ld, const StepRsrc& r, int k_lane,
                                         int v_lane) {
 #pragma unroll
   for (int s = 0; s < Geometry<D>::KS; ++s) {
-    ld.k0[s] = ld_b128(kb0 + k_lane + s * 64);
-    ld.k1[s] = ld_b128(kb1 + k_lane + s * 64);
+    ld.k0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + s * 64, 0, 0));
+    ld.k1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + s * 64, 0, 0));
   }
 #pragma unroll
   for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
-    ld.v0[dt] = ld_b64(vb0 + v_lane + dt * (16 * kBlock * 2));
-    ld.v1[dt] = ld_b64(vb1 + v_lane + dt * (16 * kBlock * 2));
+    ld.v0[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v0, v_lane + dt * (16 * kBlock * 2), 0, 0);
+    ld.v1[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v1, v_lane + dt * (16 * kBlock * 2), 0, 0);
   }
 }
 
@@ -279,32 +295,87 @@ __device__ inline void build_v_operand(bf16x8* vf, const StepLoads<D>& ld, int k
   }
 }
 
-struct StepBlocks {
-  const char* kb0;
-  const char* kb1;
-  const char* vb0;
-  const char* vb1;
-  bool ok0, ok1;
-};
-
-// Physical blocks of logical blocks j0 = 2*step and j0 + 1 (wave-uniform).
+// Descriptors of the two blocks of one step (wave-uniform block ids).
 template <int D>
-__device__ inline StepBlocks step_blocks(const AttnArgs& a, const int32_t* bt, int step, int nblk,
-                                         const char* kbase, const char* vbase) {
-  const int j0 = 2 * step, j1 = j0 + 1;
-  int b0 = (j0 < nblk && j0 < a.bt_stride) ? bt[j0] : -1;
-  int b1 = (j1 < nblk && j1 < a.bt_stride) ? bt[j1] : -1;
-  StepBlocks sb;
-  sb.ok0 = b0 >= 0 && b0 < a.num_blocks;
-  sb.ok1 = b1 >= 0 && b1 < a.num_blocks;
+__device__ inline StepRsrc make_step(const AttnArgs& a, int b0, int b1, const char* kbase,
+                                     const char* vbase) {
+  StepRsrc r;
+  r.ok0 = b0 >= 0 && b0 < a.num_blocks;
+  r.ok1 = b1 >= 0 && b1 < a.num_blocks;
   const int64_t stride = (int64_t)a.num_kv_heads * Geometry<D>::kHeadBytes;
-  const int64_t o0 = (sb.ok0 ? (int64_t)b0 : 0) * stride;
-  const int64_t o1 = (sb.ok1 ? (int64_t)b1 : 0) * stride;
-  sb.kb0 = kbase + o0;
-  sb.kb1 = kbase + o1;
-  sb.vb0 = vbase + o0;
-  sb.vb1 = vbase + o1;
-  return sb;
+  const int64_t o0 = (r.ok0 ? (int64_t)b0 : 0) * stride;
+  const int64_t o1 = (r.ok1 ? (int64_t)b1 : 0) * stride;
+  r.k0 = run_rsrc<D>(kbase + o0, r.ok0);
+  r.k1 = run_rsrc<D>(kbase + o1, r.ok1);
+  r.v0 = run_rsrc<D>(vbase + o0, r.ok0);
+  r.v1 = run_rsrc<D>(vbase + o1, r.ok1);
+  return r;
+}
+
+// Walks 32-token steps [s_begin, s_end) of one request for NT column tiles,
+// software-pipelined: the loads of step s+1 are in flight while step s is
+// computed, and the block ids of step s+2 are fetched with scalar loads (they
+// are wave-uniform; scalar loads are counted apart from vector loads, so they
+// never force the in-flight K/V loads to drain).  Steps whose keys all lie at
+// or below p_unmasked (and whose blocks are valid) skip the causal / tail
+// masking.
+template <int D, int NT>
+__device__ __attribute__((always_inline)) inline void walk_steps(
+    TileState<D> (&st)[NT], const bf16x8 (&qf)[NT][Geometry<D>::KS], const int (&p_col)[NT],
+    const AttnArgs& a, const int32_t* __restrict__ bt, int nblk, int s_begin, int s_end,
+    int p_unmasked, int seq_len, const char* kbase, const char* vbase, float c2) {
+  if (s_begin >= s_end) return;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int k_lane = (n * D + 8 * g) * 2;
+  const int v_lane = (n * kBlock + 4 * g) * 2;
+  const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
+  const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
+
+  // block ids of a step: always-valid addresses, validity applied after the load
+  const int lim_walk = min(lim, 2 * s_end);  // blocks past the walk are never loaded
+  auto ids_at = [&](int step) {
+    const int j0 = 2 * step, j1 = j0 + 1;
+    int b0 = bt[min(j0, last_col)];
+    int b1 = bt[min(j1, last_col)];
+    return int2{j0 < lim_walk ? b0 : -1, j1 < lim_walk ? b1 : -1};
+  };
+  auto compute = [&](const StepLoads<D>& ld, const StepRsrc& sb, int step) {
+    const int kpos = step * 2 * kBlock + 4 * g;
+    const bool mask = (step * 2 * kBlock + 2 * kBlock - 1 > p_unmasked) || !sb.ok0 || !sb.ok1;
+    bf16x8 vf[Geometry<D>::DT];
+    if (mask) {
+      build_v_operand<D, true>(vf, ld, kpos, seq_len, sb.ok0, sb.ok1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        tile_step<D, true>(st[nt], qf[nt], ld, vf, kpos, p_col[nt], sb.ok0, sb.ok1, c2);
+    } else {
+      build_v_operand<D, false>(vf, ld, kpos, seq_len, true, true);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        tile_step<D, false>(st[nt], qf[nt], ld, vf, kpos, p_col[nt], true, true, c2);
+    }
+  };
+
+  StepLoads<D> A, B;
+  int2 ids = ids_at(s_begin);
+  StepRsrc sa = make_step<D>(a, ids.x, ids.y, kbase, vbase), sbk;
+  issue_step_loads<D>(A, sa, k_lane, v_lane);
+  ids = ids_at(s_begin + 1);
+  int step = s_begin;
+  while (true) {
+    // past the end the ids are -1: zero-count descriptors, no memory traffic
+    sbk = make_step<D>(a, ids.x, ids.y, kbase, vbase);
+    ids = ids_at(step + 2);
+    issue_step_loads<D>(B, sbk, k_lane, v_lane);
+    compute(A, sa, step);
+    if (++step >= s_end) break;
+    sa = make_step<D>(a, ids.x, ids.y, kbase, vbase);
+    ids = ids_at(step + 2);
+    issue_step_loads<D>(A, sa, k_lane, v_lane);
+    compute(B, sbk, step);
+    if (++step >= s_end) break;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -323,7 +394,8 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
                            int nsplit, int max_splits, float* __restrict__ ml,
                            float* __restrict__ opart, DecodeSmem<D>& sm) {
   using Geo = Geometry<D>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n = lane & 15, g = lane >> 4;
   const int row0 = a.qsl[r];
   const int q_len = a.qsl[r + 1] - row0;
@@ -334,17 +406,16 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
   const bool col_ok = n < pairs;
   const int t = col_ok ? n / group : 0;
   const int head = kvh * group + (col_ok ? n - t * group : 0);
-  const int p_col = col_ok ? L - q_len + t : -1;
-  const int p_min = L - q_len;
+  int p_col[1] = {col_ok ? L - q_len + t : -1};
 
-  bf16x8 qf[Geo::KS];
+  bf16x8 qf[1][Geo::KS];
   {
     const char* qrow = static_cast<const char*>(a.q) +
                        ((int64_t)(row0 + t) * a.q_stride + (int64_t)head * D) * 2;
 #pragma unroll
     for (int s = 0; s < Geo::KS; ++s) {
-      qf[s] = col_ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
-                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      qf[0][s] = col_ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
+                        : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
   }
 
@@ -360,51 +431,21 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
   const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
   const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
-  const int k_lane = (n * D + 8 * g) * 2;
-  const int v_lane = (n * kBlock + 4 * g) * 2;
 
-  TileState<D> st;
-  tile_init(st);
-  if (w_begin < w_end) {
-    StepBlocks sb = step_blocks<D>(a, bt, w_begin, nblk, kbase, vbase);
-    StepLoads<D> cur;
-    issue_step_loads<D>(cur, sb.kb0, sb.kb1, sb.vb0, sb.vb1, k_lane, v_lane);
-    for (int step = w_begin; step < w_end; ++step) {
-      // prefetch the next step before computing this one
-      StepBlocks nb = sb;
-      StepLoads<D> nxt;
-      const bool more = step + 1 < w_end;
-      if (more) {
-        nb = step_blocks<D>(a, bt, step + 1, nblk, kbase, vbase);
-        issue_step_loads<D>(nxt, nb.kb0, nb.kb1, nb.vb0, nb.vb1, k_lane, v_lane);
-      }
-      const int kpos = step * 2 * kBlock + 4 * g;
-      const bool mask = (step * 2 * kBlock + 2 * kBlock - 1 > p_min) || !sb.ok0 || !sb.ok1;
-      bf16x8 vf[Geo::DT];
-      if (mask) {
-        build_v_operand<D, true>(vf, cur, kpos, L, sb.ok0, sb.ok1);
-        tile_step<D, true>(st, qf, cur, vf, kpos, p_col, sb.ok0, sb.ok1, c2);
-      } else {
-        build_v_operand<D, false>(vf, cur, kpos, L, true, true);
-        tile_step<D, false>(st, qf, cur, vf, kpos, p_col, true, true, c2);
-      }
-      if (more) {
-        cur = nxt;
-        sb = nb;
-      }
-    }
-  }
+  TileState<D> st[1];
+  tile_init(st[0]);
+  walk_steps<D, 1>(st, qf, p_col, a, bt, nblk, w_begin, w_end, L - q_len, L, kbase, vbase, c2);
 
   // merge the four waves' states
-  float l_tot = st.l + __shfl_xor(st.l, 16, 64);
+  float l_tot = st[0].l + __shfl_xor(st[0].l, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (g == 0) {
-    sm.m[wave][n] = st.m;
+    sm.m[wave][n] = st[0].m;
     sm.l[wave][n] = l_tot;
   }
 #pragma unroll
   for (int dt = 0; dt < Geo::DT; ++dt)
-    *reinterpret_cast<f32x4*>(&sm.o[wave][n][16 * dt + 4 * g]) = st.o[dt];
+    *reinterpret_cast<f32x4*>(&sm.o[wave][n][16 * dt + 4 * g]) = st[0].o[dt];
   __syncthreads();
 
   constexpr int kDimsPerThread = D / 16;  // 256 threads = 16 columns x 16 dim chunks
@@ -470,7 +511,8 @@ template <int D>
 __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int kvh, int mtile) {
   using Geo = Geometry<D>;
   constexpr int NT = kPrefillTilesPerWave;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n = lane & 15, g = lane >> 4;
   const int row0 = a.qsl[r];
   const int q_len = a.qsl[r + 1] - row0;
@@ -506,32 +548,11 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
   const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
-  const int k_lane = (n * D + 8 * g) * 2;
-  const int v_lane = (n * kBlock + 4 * g) * 2;
 
   TileState<D> st[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) tile_init(st[nt]);
-
-  for (int step = 0; step < nsteps; ++step) {
-    const StepBlocks sb = step_blocks<D>(a, bt, step, nblk, kbase, vbase);
-    StepLoads<D> ld;
-    issue_step_loads<D>(ld, sb.kb0, sb.kb1, sb.vb0, sb.vb1, k_lane, v_lane);
-    const int kpos = step * 2 * kBlock + 4 * g;
-    const bool mask = (step * 2 * kBlock + 2 * kBlock - 1 > p_lo) || !sb.ok0 || !sb.ok1;
-    bf16x8 vf[Geo::DT];
-    if (mask) {
-      build_v_operand<D, true>(vf, ld, kpos, L, sb.ok0, sb.ok1);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        tile_step<D, true>(st[nt], qf[nt], ld, vf, kpos, p_col[nt], sb.ok0, sb.ok1, c2);
-    } else {
-      build_v_operand<D, false>(vf, ld, kpos, L, true, true);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        tile_step<D, false>(st[nt], qf[nt], ld, vf, kpos, p_col[nt], true, true, c2);
-    }
-  }
+  walk_steps<D, NT>(st, qf, p_col, a, bt, nblk, 0, nsteps, p_lo, L, kbase, vbase, c2);
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
