@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--rows", default="all", choices=["all", "decode", "prefill"],
+                   help="time the whole batch, or only its single-token/short (decode) "
+                        "or prompt-chunk (prefill) requests over the same pools")
     p.add_argument("--split-tokens", type=int, default=0,
                    help="context partition size of decode items (0 = library default)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -137,6 +140,14 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = workloads.config(args.workload, device=dev)
+    if args.rows != "all":
+        group = wl.num_q_heads // wl.num_kv_heads
+        short = wl.num_scheduled_tokens * group <= 16
+        keep = np.nonzero(short if args.rows == "decode" else ~short)[0]
+        if len(keep) == 0:
+            print(f"workload {args.workload} has no {args.rows} rows", file=sys.stderr)
+            sys.exit(2)
+        wl = workloads.select(wl, keep)
     work = algorithmic_work(wl)
     T, R = wl.num_tokens, wl.num_reqs
     nst = torch.from_numpy(wl.num_scheduled_tokens).to(dev)
@@ -222,7 +233,7 @@ def main():
                    "num_tokens": T, "context_tokens": work["context_tokens"],
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "seed": wl.seed,
-                   "split_tokens": args.split_tokens},
+                   "split_tokens": args.split_tokens, "rows": args.rows},
         "phases_ms": {"prepare": round(t_prep, 4), "kv_write": round(t_write, 4),
                       "attention": round(t_attn, 4)},
         "context_tokens_per_s": round(work["context_tokens"] / (ms_step / 1e3), 1),

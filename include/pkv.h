@@ -197,7 +197,8 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
  *   num_q_heads, num_kv_heads  host; num_q_heads % num_kv_heads == 0
  *   head_dim        host, 64 or 128
  *   block_size      host, 16
- *   scale           host, the softmax scale (1/sqrt(head_dim) for plain models)
+ *   scale           host, the softmax scale (1/sqrt(head_dim) for plain models),
+ *                   finite and > 0
  *   dtype           PKV_BF16 (MFMA path) or PKV_F32 (fp32 vector path)
  *   split_tokens    host, partition size (tokens) for splitting one long
  *                   decode context over several workgroups; 0 = automatic;
@@ -212,7 +213,7 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
  * rounded to nearest even.
  * Errors: PKV_ERR_INVALID_ARG (null pointers, sizes, num_q_heads not a
  * multiple of num_kv_heads, row strides too small, split_tokens not a
- * multiple of 32); PKV_ERR_UNSUPPORTED (head_dim not 64/128, block_size not
+ * multiple of 32, scale not finite and positive); PKV_ERR_UNSUPPORTED (head_dim not 64/128, block_size not
  * 16, more than 16 q heads per kv head); PKV_ERR_WORKSPACE; PKV_ERR_LAUNCH.
  */
 pkv_status pkv_paged_attention_varlen(

@@ -1,6 +1,7 @@
 // api.hip -- the extern "C" entry points of libpkv (declared in include/pkv.h).
 // Host-side validation of scalar arguments, then kernel launches on the
 // caller's stream.  Nothing here reads device memory or allocates.
+#include <math.h>
 #include <stdint.h>
 
 #include "pkv_internal.h"
@@ -98,6 +99,7 @@ pkv_status pkv_paged_attention_varlen(
       split_tokens < 0 || split_tokens % 32 != 0)
     return PKV_ERR_INVALID_ARG;
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == HUGE_VALF) return PKV_ERR_INVALID_ARG;  // also rejects NaN
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (block_size != pkv::kBlock) return PKV_ERR_UNSUPPORTED;
   const int32_t group = num_q_heads / num_kv_heads;

@@ -504,13 +504,76 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
 }
 
 // ---------------------------------------------------------------------------
-// prefill item
+// prefill item: K/V staged in LDS, shared by the four waves
 // ---------------------------------------------------------------------------
+//
+// One item = 128 (row, head) pairs of one request and kv head; wave w owns
+// pairs [32w, 32w + 32) as two 16-column MFMA tiles.  The context is walked in
+// 64-token steps (4 blocks).  Each step's K and V runs are fetched once per
+// workgroup -- wave w fetches block w of the step through its buffer
+// descriptors -- into registers while the previous step is computed, then
+// written to the other half of a double-buffered LDS tile; one barrier per
+// step.
+//
+// QK^T tile t of a step is block t (MFMA row m = token m of the block).  After
+// S^T = K Q^T the lane group g of a column holds tokens 4g .. 4g+3 of blocks
+// 2k and 2k+1, which is the P^T operand of PV k-step k; the V^T operand of a
+// lane is the matching 4 + 4 tokens of one dim.
+// LDS layouts are "operand-major": the 16 lanes of a lane group that read
+// one MFMA operand fragment read one contiguous, aligned 256-byte run, which
+// the gfx950 LDS serves without bank conflicts (spreading a 16-lane group
+// over several rows costs extra cycles, measured with the LDS bank-conflict
+// counter).  Every operand read is 16*lane or a lane base plus an immediate:
+//  * K:   [block t][8-dim chunk c][16 tokens] x 16 bytes;
+//  * V^T: [k-step k][16-dim tile][lane group g][16 dims] x 16 bytes, each 16
+//    bytes = tokens 4g..4g+3 of block 2k, then of block 2k+1.
+// The staging loads pick, per lane, the global 16-byte chunk whose LDS slot
+// makes each 16-lane write group fill one 256-byte segment as well.
+// The softmax denominator is accumulated by one more MFMA per PV k-step, with
+// an all-ones A operand: it sums exactly the bf16-rounded weights that the
+// numerator uses.
+
+constexpr int kPrefillStep = 64;  // tokens per prefill step (4 blocks)
+constexpr float kLazyLog2 = 16.f;  // rescale when a column max grows by > 2^16
 
 template <int D>
-__device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int kvh, int mtile) {
+struct PrefillLayout {
+  static constexpr int kBytes = kPrefillStep * D * 2;  // one K buffer
+  static constexpr int vBytes = kPrefillStep * D * 2;  // one V buffer
+  static constexpr int kOff0 = 0, kOff1 = kBytes;
+  static constexpr int vOff0 = 2 * kBytes, vOff1 = 2 * kBytes + vBytes;
+  static constexpr int total = 2 * kBytes + 2 * vBytes;
+};
+
+template <int D>
+struct PrefillSmem {
+  char bytes[PrefillLayout<D>::total];
+};
+
+// Zero element e of an 8 x bf16 run when first + e >= limit.
+__device__ inline u32x4 keep_below(u32x4 v, int first, int limit) {
+  unsigned m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned lo = (first + 2 * i < limit) ? 0x0000FFFFu : 0u;
+    const unsigned hi = (first + 2 * i + 1 < limit) ? 0xFFFF0000u : 0u;
+    m[i] = lo | hi;
+  }
+  return u32x4{v.x & m[0], v.y & m[1], v.z & m[2], v.w & m[3]};
+}
+
+template <typename T>
+__device__ inline T lds_ld(const char* base, int off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
+template <int D>
+__device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int kvh, int mtile,
+                            PrefillSmem<D>& sm) {
   using Geo = Geometry<D>;
+  using Lay = PrefillLayout<D>;
   constexpr int NT = kPrefillTilesPerWave;
+  constexpr int KQ = (int)(Geo::kHeadBytes / 1024);  // 16-byte loads per lane per run
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n = lane & 15, g = lane >> 4;
@@ -518,8 +581,9 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   const int q_len = a.qsl[r + 1] - row0;
   const int L = a.seq_lens[r];
   const int pairs = q_len * group;
-  const int pbase = mtile * kPrefillPairs + wave * (NT * kPairsPerTile);
-  if (pbase >= pairs) return;  // this wave has no rows (no barrier follows)
+  const int tile_base = mtile * kPrefillPairs;
+  const int pbase = tile_base + wave * (NT * kPairsPerTile);
+  const bool wave_has_rows = pbase < pairs;
 
   bf16x8 qf[NT][Geo::KS];
   int p_col[NT];
@@ -538,26 +602,199 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
                      : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
   }
-  const int t_lo = pbase / group;
-  const int t_hi = (min(pairs, pbase + NT * kPairsPerTile) - 1) / group;
+  // rows seen by this wave and by the whole workgroup
+  const int t_lo = wave_has_rows ? pbase / group : 0;
+  const int t_hi = wave_has_rows ? (min(pairs, pbase + NT * kPairsPerTile) - 1) / group : -1;
   const int p_lo = L - q_len + t_lo;
-  const int p_hi = L - q_len + t_hi;
-  const int nblk = L > 0 ? ceil_div(L, kBlock) : 0;
-  const int nsteps = p_hi >= 0 ? min(ceil_div(nblk, 2), p_hi / (2 * kBlock) + 1) : 0;
+  const int p_hi = wave_has_rows ? L - q_len + t_hi : -1;
+  const int wg_last = (min(pairs, tile_base + kPrefillPairs) - 1) / group;
+  const int p_hi_wg = L - q_len + wg_last;
+  const int nsteps = p_hi_wg >= 0 ? min(ceil_div(L, kPrefillStep), p_hi_wg / kPrefillStep + 1)
+                                   : 0;
 
-  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const int32_t* __restrict__ bt = a.block_table + (int64_t)r * a.bt_stride;
   const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::kHeadBytes;
+  const int nblk = L > 0 ? ceil_div(L, kBlock) : 0;
+  const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
+  const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
+
+  // validity of the 4 blocks of a step (bit b = block b is inside the context
+  // and its id lies in the pool); scalar loads, branch-free
+  auto step_valid = [&](int step) {
+    unsigned bits = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = 4 * step + b;
+      const int id = bt[min(j, last_col)];
+      bits |= (j < lim && id >= 0 && id < a.num_blocks) ? (1u << b) : 0u;
+    }
+    return bits;
+  };
+
+  // lane-constant offsets of the staging loads and writes.  K load q of lane
+  // (m = lane & 15, c = 4q + (lane >> 4)) moves dims 8c..8c+7 of token m; V
+  // load q moves tokens 8h..8h+7 of dim 16*dt + (lane & 15), where
+  // 2*dt + h = 4q + (lane >> 4), and is written as two 8-byte halves.
+  int k_src[KQ], k_st[KQ], v_src[KQ], v_st[KQ], v_half[KQ];
+#pragma unroll
+  for (int q = 0; q < KQ; ++q) {
+    const int m = lane & 15, c = 4 * q + (lane >> 4);
+    k_src[q] = m * 2 * D + 16 * c;
+    k_st[q] = ((wave * (D / 8) + c) * 16 + m) * 16;
+    const int grp = 4 * q + (lane >> 4), dt = grp >> 1, h = grp & 1;
+    v_src[q] = (16 * dt + (lane & 15)) * 2 * kBlock + 16 * h;
+    v_st[q] = (((wave >> 1) * (D / 16) + dt) * 4 + 2 * h) * 256 + (lane & 15) * 16 + 8 * (wave & 1);
+    v_half[q] = h;
+  }
+  // this wave's fetch of block `wave` of a step into registers (a block past
+  // the context or the walk gets a zero-count descriptor: no memory traffic)
+  u32x4 rk[KQ], rv[KQ];
+  auto fetch = [&](int step) {
+    const int j = 4 * step + wave;
+    const int id = bt[min(j, last_col)];
+    const bool ok = j < lim && step < nsteps && id >= 0 && id < a.num_blocks;
+    const int64_t off = (ok ? (int64_t)id : 0) * blk_stride;
+    const rsrc_t rk_d = run_rsrc<D>(kbase + off, ok);
+    const rsrc_t rv_d = run_rsrc<D>(vbase + off, ok);
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      rk[q] = __builtin_amdgcn_raw_buffer_load_b128(rk_d, k_src[q], 0, 0);
+      rv[q] = __builtin_amdgcn_raw_buffer_load_b128(rv_d, v_src[q], 0, 0);
+    }
+  };
+  // write the fetched runs into LDS buffer `buf`; V tokens past the context are
+  // zeroed here (their probability is 0, but the pool may hold NaN there)
+  auto stage = [&](int step, int buf) {
+    char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0);
+    char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0);
+    const int tok0 = step * kPrefillStep + wave * kBlock;  // first token of this block
+    const bool tail = tok0 + kBlock > L;
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      *reinterpret_cast<u32x4*>(kb + k_st[q]) = rk[q];
+      u32x4 v = rv[q];
+      if (tail) v = keep_below(v, tok0 + 8 * v_half[q], L);
+      *reinterpret_cast<u32x2*>(vb + v_st[q]) = u32x2{v.x, v.y};
+      *reinterpret_cast<u32x2*>(vb + v_st[q] + 256) = u32x2{v.z, v.w};
+    }
+  };
+  // lane-constant LDS offsets of the MFMA operand reads
+  const int k_rd = 16 * lane;  // + immediates for tile / k-step
+  const int v_rd = 16 * lane;  // + immediates for k-step / dim tile
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                       0x3F803F80u});
 
   TileState<D> st[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) tile_init(st[nt]);
-  walk_steps<D, NT>(st, qf, p_col, a, bt, nblk, 0, nsteps, p_lo, L, kbase, vbase, c2);
-
+  f32x4 lacc[NT];   // softmax denominators (every row of a column holds the same sum)
+  float mref[NT];   // m * c2 of the reference max, 0 while a column has no key yet
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float l_tot = st[nt].l + __shfl_xor(st[nt].l, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    tile_init(st[nt]);
+    lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mref[nt] = 0.f;
+  }
+
+  fetch(0);
+  stage(0, 0);
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    fetch(step + 1);
+    if (step * kPrefillStep <= p_hi) {
+      const char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + k_rd;
+      const char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + v_rd;
+      const unsigned valid = step_valid(step);
+      const bool mask = (step * kPrefillStep + kPrefillStep - 1 > p_lo) || valid != 0xFu;
+      // S^T = K Q^T for the 4 token tiles of the step
+      f32x4 sacc[NT][4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        bf16x8 kf[Geo::KS];
+#pragma unroll
+        for (int s = 0; s < Geo::KS; ++s)
+          kf[s] = lds_ld<bf16x8>(kb, (tt * (D / 8) + 4 * s) * 256);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < Geo::KS; ++s) acc = mfma_bf16(kf[s], qf[nt][s], acc);
+          sacc[nt][tt] = acc;
+        }
+      }
+      // softmax weights, P^T packed for the PV MFMA.  The reference max is
+      // refreshed only when some column's max grows by more than 2^kLazyLog2
+      // (then O and the denominator are rescaled); otherwise the stale
+      // reference is kept and the weights stay <= 2^kLazyLog2.  Numerator and
+      // denominator share the reference, so the result is unchanged.
+      bf16x8 pf[NT][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (mask) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int tok = 16 * tt + 4 * g;  // + i
+            const bool bok = (valid >> tt) & 1u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kpos = step * kPrefillStep + tok + i;
+              sacc[nt][tt][i] = (bok && kpos <= p_col[nt]) ? sacc[nt][tt][i] : -INFINITY;
+            }
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          mx = fmaxf(fmaxf(mx, fmaxf(sacc[nt][tt][0], sacc[nt][tt][1])),
+                     fmaxf(sacc[nt][tt][2], sacc[nt][tt][3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // the first key a column sees sets its reference; later ones move it
+        // only when the max grows by more than 2^kLazyLog2
+        const bool first = st[nt].m == -INFINITY && mx != -INFINITY;
+        const bool grow = first || mx * c2 > mref[nt] + kLazyLog2;
+        if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+          const float m_new = grow ? fmaxf(st[nt].m, mx) : st[nt].m;
+          const float r_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
+          const float alpha = (st[nt].m == -INFINITY) ? 0.f : fast_exp2(mref[nt] - r_new);
+          lacc[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < Geo::DT; ++dt) st[nt].o[dt] *= alpha;
+          st[nt].m = m_new;
+          mref[nt] = r_new;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pf[nt][kk][i] = static_cast<__bf16>(fast_exp2(fmaf(sacc[nt][2 * kk][i], c2, -mref[nt])));
+            pf[nt][kk][4 + i] =
+                static_cast<__bf16>(fast_exp2(fmaf(sacc[nt][2 * kk + 1][i], c2, -mref[nt])));
+          }
+        }
+      }
+      // O^T += V^T P^T, and the denominators
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma_bf16(ones, pf[nt][kk], lacc[nt]);
+#pragma unroll
+        for (int dt = 0; dt < Geo::DT; ++dt) {
+          const bf16x8 vf = lds_ld<bf16x8>(vb, (kk * (D / 16) + dt) * 4 * 256);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) st[nt].o[dt] = mfma_bf16(vf, pf[nt][kk], st[nt].o[dt]);
+        }
+      }
+    }
+    stage(step + 1, buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_has_rows) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float l_tot = lacc[nt][0];
     const int P = pbase + nt * kPairsPerTile + n;
     if (P < pairs) {
       const int t = P / group;
@@ -577,17 +814,26 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_main_kernel(
+union MainSmem {
+  DecodeSmem<D> dec;
+  PrefillSmem<D> pre;
+};
+
+// Two workgroups per CU (2 waves per SIMD, <= 256 registers per lane): one
+// wave's softmax VALU work overlaps the other's MFMAs, and a decode item's
+// start-up latency overlaps the other workgroup's loads.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_main_kernel(
     AttnArgs a, int32_t group, float c2, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items, int32_t max_splits, float* __restrict__ ml,
     float* __restrict__ opart) {
-  __shared__ DecodeSmem<D> sm;
+  __shared__ MainSmem<D> sm;
   if ((int)blockIdx.x >= *n_items) return;
   const int4 it = items[blockIdx.x];
   if (it.w < 0)
-    run_prefill<D>(a, group, c2, it.x, it.y, it.z);
+    run_prefill<D>(a, group, c2, it.x, it.y, it.z, sm.pre);
   else
-    run_decode<D>(a, group, c2, it.x, it.y, it.z, it.w, max_splits, ml, opart, sm);
+    run_decode<D>(a, group, c2, it.x, it.y, it.z, it.w, max_splits, ml, opart, sm.dec);
 }
 
 // ---------------------------------------------------------------------------

@@ -12,8 +12,8 @@ namespace pkv {
 constexpr int kBlock = 16;          // tokens per KV block the attention kernels read
 constexpr int kPairsPerTile = 16;   // MFMA N width: (query row, q head) pairs per tile
 constexpr int kWaves = 4;           // waves per attention workgroup
-constexpr int kPrefillTilesPerWave = 4;  // 16-pair tiles one wave owns in a prefill item
-constexpr int kPrefillPairs = kWaves * kPrefillTilesPerWave * kPairsPerTile;  // 256
+constexpr int kPrefillTilesPerWave = 2;  // 16-pair tiles one wave owns in a prefill item
+constexpr int kPrefillPairs = kWaves * kPrefillTilesPerWave * kPairsPerTile;  // 128
 
 // Host-side plan of one attention call (derived from host scalars only).
 struct AttnPlan {

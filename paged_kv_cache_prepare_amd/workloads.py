@@ -192,6 +192,27 @@ def build(name: str, nst, nct, *, num_q_heads: int, num_kv_heads: int, head_dim:
     return wl
 
 
+def select(wl: Workload, reqs, name: str | None = None) -> Workload:
+    """The sub-batch of requests ``reqs`` (in order) over the same block pools:
+    their scheduled rows of Q/K/V, counts and block-table rows."""
+    reqs = np.asarray(reqs, dtype=np.int64)
+    starts = np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)]).astype(np.int64)
+    rows = np.concatenate([np.arange(starts[r], starts[r + 1]) for r in reqs]) if len(reqs) \
+        else np.zeros(0, np.int64)
+    idx = torch.from_numpy(rows).to(wl.q.device)
+    sub = Workload(name=name or f"{wl.name}[{len(reqs)} requests]",
+                   num_scheduled_tokens=wl.num_scheduled_tokens[reqs].copy(),
+                   num_computed_tokens=wl.num_computed_tokens[reqs].copy(),
+                   block_table=np.ascontiguousarray(wl.block_table[reqs]),
+                   num_blocks=wl.num_blocks, num_q_heads=wl.num_q_heads,
+                   num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
+                   block_size=wl.block_size, dtype=wl.dtype, scale=wl.scale, seed=wl.seed,
+                   q=wl.q[idx].contiguous(), key=wl.key[idx].contiguous(),
+                   value=wl.value[idx].contiguous(), key_cache=wl.key_cache,
+                   value_cache=wl.value_cache, notes=dict(wl.notes))
+    return sub
+
+
 # ---------------------------------------------------------------------------
 # The five named configurations
 # ---------------------------------------------------------------------------

@@ -98,6 +98,9 @@ def attn(lib, **kw):
     (dict(Hq=6, Hkv=4), binding.ERR_INVALID_ARG), (dict(R=-1), binding.ERR_INVALID_ARG),
     (dict(split=48), binding.ERR_INVALID_ARG), (dict(split=-32), binding.ERR_INVALID_ARG),
     (dict(dt=3), binding.ERR_INVALID_ARG), (dict(d=96), binding.ERR_UNSUPPORTED),
+    (dict(scale=0.0), binding.ERR_INVALID_ARG), (dict(scale=-0.1), binding.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), binding.ERR_INVALID_ARG),
     (dict(bs=32), binding.ERR_UNSUPPORTED), (dict(Hq=64, Hkv=2), binding.ERR_UNSUPPORTED),
     (dict(q=None), binding.ERR_INVALID_ARG), (dict(qs=100), binding.ERR_INVALID_ARG),
     (dict(out=FAKE + 8), binding.ERR_INVALID_ARG), (dict(bts=0), binding.ERR_INVALID_ARG),

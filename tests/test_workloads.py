@@ -46,3 +46,13 @@ def test_large_config_structures():
     s5 = workloads.config_structure(5)
     assert s5["num_scheduled_tokens"].sum() == 2064
     assert (s5["num_computed_tokens"][:16] + 1 == 32768).all()
+
+
+def test_select_keeps_rows_of_chosen_requests():
+    wl = workloads.build("t", [3, 1, 2], [5, 9, 0], num_q_heads=4, num_kv_heads=2, head_dim=8,
+                         seed=4)
+    sub = workloads.select(wl, [2, 0])
+    assert sub.num_scheduled_tokens.tolist() == [2, 3]
+    assert np.array_equal(sub.block_table, wl.block_table[[2, 0]])
+    assert torch.equal(sub.q, torch.cat([wl.q[4:6], wl.q[0:3]]))
+    assert sub.key_cache is wl.key_cache
