@@ -49,7 +49,31 @@ def parse():
                    help="context partition size of decode items (0 = library default)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate budget of the CPU oracle baseline")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="instead of the step, time a plain device-to-device copy of this many "
+                        "MiB (the known-size kernel that HBM byte counters are scaled by)")
     return p.parse_args()
+
+
+def copy_probe(mib, launches=10):
+    """Device-to-device copy of a known size: reads and writes ``mib`` MiB per launch."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(launches):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize(dev)
+    ms = ev[0].elapsed_time(ev[1]) / launches
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": launches + 1,
+                      "ms_per_copy": round(ms, 4), "copy_gbs": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
 
 
 def algorithmic_work(wl):
@@ -134,6 +158,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+        return
     import torch
     import paged_kv_cache_prepare_amd as pkv
     from paged_kv_cache_prepare_amd import workloads

@@ -10,9 +10,9 @@
 //
 // bf16 path (three launches per call, all on the caller's stream):
 //  1. plan:   one workgroup turns query_start_loc / seq_lens into a work list
-//             in the workspace: prefill tiles first (latest rows first, since
-//             they see the most keys), then decode items.  Host code never
-//             reads device data, so the list is built on the device.
+//             in the workspace: prefill tiles first, then decode partitions,
+//             longest contexts first.  Host code never reads device data, so
+//             the list is built on the device.
 //  2. main:   one workgroup (4 waves) per work item; prompt-chunk tiles and
 //             single-token decodes of the same step run in this one launch.
 //             * decode item = (request, kv head, partition): the q heads of
@@ -20,9 +20,9 @@
 //               form the 16-wide N side of v_mfma_f32_16x16x32_bf16; the 4
 //               waves split the partition's 32-token steps and merge their
 //               (max, sum, acc) states through LDS at the end.
-//             * prefill item = (request, kv head, 256 (row, head) pairs): each
-//               wave owns 64 pairs (4 MFMA N tiles) and walks every key step
-//               its rows can see.
+//             * prefill item = (request, kv head, 128 (row, head) pairs): each
+//               wave owns 32 pairs (2 MFMA N tiles); the workgroup stages each
+//               64-token K/V step in LDS once for all four waves.
 //             Both walk the context two 16-token blocks at a time: K rows are
 //             the MFMA A operand (16 tokens x 32 dims per load); S^T = K Q^T
 //             lands with 4 tokens of one column per lane, which is exactly
@@ -113,43 +113,176 @@ __device__ inline int block_scan_1024(int v, int* wave_tot, int* total) {
   return v + before;
 }
 
-__global__ __launch_bounds__(1024) void attn_plan_kernel(
+// First index in the non-decreasing s[0..n) whose value exceeds x (n if none).
+__device__ inline int upper_bound_lds(const int* s, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s[mid] > x) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// First index in the non-increasing s[0..n) whose value is <= x (n if none).
+__device__ inline int first_not_above(const int* s, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s[mid] <= x) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+struct PlanSmem {
+  int wave[16];
+  int len[kPlanReqs];    // seq_len by request (ordered path)
+  int req[kPlanReqs];    // request at rank j (ordered path) / unused (chunked path)
+  int incl[kPlanReqs];   // inclusive prefix of per-slot unit counts
+  int aux[kPlanReqs];    // per-slot split count or tile count
+  int dreq[kPlanReqs];   // decode requests in rank order
+  int dns[kPlanReqs];    // their split counts (non-increasing)
+  int pk[kPlanMaxSplits + 1];  // decode units before split index k
+};
+
+// Work units of one request in a pass: prefill tiles (pass 0) or decode
+// partitions (pass 1).  *aux gets the tile count or the split count.
+__device__ inline int plan_units(const int32_t* qsl, const int32_t* seq_lens, int r,
+                                 int num_tokens, int group, int split_tokens, int max_splits,
+                                 int pass, int* aux) {
+  const int pairs = valid_q_len(qsl, r, num_tokens) * group;
+  int cnt = 0;
+  if (pass == 0 && pairs > kPairsPerTile) cnt = ceil_div(pairs, kPrefillPairs);
+  if (pass == 1 && pairs >= 1 && pairs <= kPairsPerTile)
+    cnt = num_splits(seq_lens[r], split_tokens, max_splits);
+  *aux = cnt;
+  return cnt;
+}
+
+// The work list.  Item = (request, kv head, index, split count): index is the
+// row tile of a prefill item (split count -1) or the partition of a decode
+// item.  Items of one unit (a tile or a partition) are consecutive, one per kv
+// head.  Prefill units come first, then decode units.
+//
+// Ordered path (num_reqs <= kPlanReqs and max_splits <= kPlanMaxSplits):
+// requests are ranked by seq_len, longest first, so the longest work starts
+// first and the tail of the launch holds the short items.  Prefill tiles of a
+// request go latest rows first (they see the most keys).  Decode units go
+// partition-major: partition 0 of every request, then partition 1, ...; the
+// later partitions of a context are its shorter remainders, and requests that
+// share prefix blocks read those blocks at about the same time.
+// Chunked path (larger batches): request order, 1024 requests per scan.
+__global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t num_reqs,
     int32_t num_tokens, int32_t num_kv_heads, int32_t group, int32_t split_tokens, int32_t max_splits,
     int64_t max_items, int4* __restrict__ items, int32_t* __restrict__ n_items) {
-  __shared__ int s_wave[16];
+  __shared__ PlanSmem sm;
   const int tid = threadIdx.x;
-  int64_t carry = 0;  // work items emitted so far (in units of kv-head groups)
-  // pass 1: prefill tiles, pass 2: decode items
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int base = 0; base < num_reqs; base += 1024) {
-      const int r = base + tid;
-      int cnt = 0, nsplit = 0;
-      if (r < num_reqs) {
-        const int q_len = valid_q_len(qsl, r, num_tokens);
-        const int pairs = q_len * group;
-        if (pass == 0 && pairs > kPairsPerTile) cnt = ceil_div(pairs, kPrefillPairs);
-        if (pass == 1 && pairs >= 1 && pairs <= kPairsPerTile) {
-          nsplit = num_splits(seq_lens[r], split_tokens, max_splits);
-          cnt = nsplit;
-        }
+  const int H = num_kv_heads;
+  int64_t carry = 0;  // units emitted so far; item index = unit * H + kv head
+  const bool ordered = num_reqs <= kPlanReqs && max_splits <= kPlanMaxSplits;
+
+  if (ordered) {
+    const int L = tid < num_reqs ? seq_lens[tid] : 0;
+    if (tid < num_reqs) sm.len[tid] = L;
+    __syncthreads();
+    if (tid < num_reqs) {
+      int rank = 0;
+      for (int j = 0; j < num_reqs; ++j) {
+        const int Lj = sm.len[j];
+        rank += (Lj > L || (Lj == L && j < tid)) ? 1 : 0;
       }
+      sm.req[rank] = tid;
+    }
+    __syncthreads();
+    // pass 0: prefill tiles, in rank order
+    {
+      int tiles = 0;
+      if (tid < num_reqs)
+        plan_units(qsl, seq_lens, sm.req[tid], num_tokens, group, split_tokens, max_splits, 0,
+                   &tiles);
       int total;
-      const int incl = block_scan_1024(cnt, s_wave, &total);
-      const int64_t first = carry + incl - cnt;
-      for (int k = 0; k < cnt; ++k) {
-        for (int h = 0; h < num_kv_heads; ++h) {
-          const int64_t idx = (first + k) * num_kv_heads + h;
-          if (idx >= max_items) break;
-          // prefill: latest tile first; decode: partition k of nsplit
-          items[idx] = pass == 0 ? make_int4(r, h, cnt - 1 - k, -1) : make_int4(r, h, k, nsplit);
-        }
+      const int incl = block_scan_1024(tiles, sm.wave, &total);
+      sm.incl[tid] = incl;
+      sm.aux[tid] = tiles;
+      __syncthreads();
+      const int64_t n = (int64_t)total * H;
+      for (int64_t e = tid; e < n; e += kPlanReqs) {
+        if (e >= max_items) break;
+        const int u = (int)(e / H), h = (int)(e - (int64_t)u * H);
+        const int j = upper_bound_lds(sm.incl, num_reqs, u);
+        const int k = u - (sm.incl[j] - sm.aux[j]);
+        items[e] = make_int4(sm.req[j], h, sm.aux[j] - 1 - k, -1);
       }
-      carry += total;
+      carry = total;
+    }
+    // pass 1: decode partitions, partition-major over the decode requests in rank order
+    {
+      int ns = 0;
+      if (tid < num_reqs)
+        plan_units(qsl, seq_lens, sm.req[tid], num_tokens, group, split_tokens, max_splits, 1, &ns);
+      int nd;
+      const int ci = block_scan_1024(ns > 0 ? 1 : 0, sm.wave, &nd) - 1;
+      if (ns > 0) {
+        sm.dreq[ci] = sm.req[tid];
+        sm.dns[ci] = ns;
+      }
+      __syncthreads();
+      // units with partition index k: decode requests whose split count exceeds k
+      int pcarry = 0;
+      for (int kb = 0; kb < max_splits; kb += kPlanReqs) {
+        const int k = kb + tid;
+        const int ck = k < max_splits ? first_not_above(sm.dns, nd, k) : 0;
+        int tot;
+        const int incl = block_scan_1024(ck, sm.wave, &tot);
+        if (k < max_splits) sm.pk[k + 1] = pcarry + incl;
+        pcarry += tot;
+      }
+      if (tid == 0) sm.pk[0] = 0;
+      __syncthreads();
+      const int64_t base = carry * H;
+      const int64_t n = (int64_t)pcarry * H;
+      for (int64_t e = tid; e < n; e += kPlanReqs) {
+        const int64_t idx = base + e;
+        if (idx >= max_items) break;
+        const int u = (int)(e / H), h = (int)(e - (int64_t)u * H);
+        const int k = upper_bound_lds(sm.pk, max_splits + 1, u) - 1;
+        const int j = u - sm.pk[k];
+        items[idx] = make_int4(sm.dreq[j], h, k, sm.dns[j]);
+      }
+      carry += pcarry;
+    }
+  } else {
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int rb = 0; rb < num_reqs; rb += kPlanReqs) {
+        const int r = rb + tid;
+        int cnt = 0, aux = 0;
+        if (r < num_reqs)
+          cnt = plan_units(qsl, seq_lens, r, num_tokens, group, split_tokens, max_splits, pass,
+                           &aux);
+        int total;
+        const int incl = block_scan_1024(cnt, sm.wave, &total);
+        sm.incl[tid] = incl;
+        sm.aux[tid] = aux;
+        __syncthreads();
+        const int nslot = min(kPlanReqs, num_reqs - rb);
+        const int64_t base = carry * H;
+        const int64_t n = (int64_t)total * H;
+        for (int64_t e = tid; e < n; e += kPlanReqs) {
+          const int64_t idx = base + e;
+          if (idx >= max_items) break;
+          const int u = (int)(e / H), h = (int)(e - (int64_t)u * H);
+          const int j = upper_bound_lds(sm.incl, nslot, u);
+          const int k = u - (sm.incl[j] - sm.aux[j]);
+          items[idx] = pass == 0 ? make_int4(rb + j, h, sm.aux[j] - 1 - k, -1)
+                                 : make_int4(rb + j, h, k, sm.aux[j]);
+        }
+        carry += total;
+        __syncthreads();  // incl / aux are rewritten by the next chunk
+      }
     }
   }
   if (tid == 0) {
-    const int64_t n = carry * num_kv_heads;
+    const int64_t n = carry * H;
     *n_items = (int32_t)(n < max_items ? n : max_items);
   }
 }
@@ -973,7 +1106,7 @@ hipError_t launch_bf16_d(const AttnArgs& a, const AttnPlan& plan, void* workspac
   float* ml = plan.max_splits > 1 ? reinterpret_cast<float*>(ws + plan.ml_offset) : nullptr;
   float* opart = plan.max_splits > 1 ? reinterpret_cast<float*>(ws + plan.o_offset) : nullptr;
   const float c2 = a.scale * kLog2e;
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.seq_lens,
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanReqs), 0, stream, a.qsl, a.seq_lens,
                      a.num_reqs, a.num_tokens, a.num_kv_heads, plan.group, plan.split_tokens, plan.max_splits,
                      plan.max_items, items, n_items);
   hipError_t e = hipGetLastError();
@@ -1023,8 +1156,12 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
   p.split_tokens = st;
   p.max_splits = std::max(1, (std::max(max_seq_len, 1) + st - 1) / st);
   const int64_t g = p.group;
-  const int64_t prefill_tiles = ((int64_t)num_tokens * g + kPrefillPairs - 1) / kPrefillPairs +
-                                num_reqs;
+  // A prefill request has q_len * G > 16, so at most T / (16 / G + 1) requests
+  // are prefill requests; each adds at most one partial tile.
+  const int64_t min_prefill_q = kPairsPerTile / g + 1;
+  const int64_t prefill_reqs = std::min<int64_t>(num_reqs, num_tokens / min_prefill_q);
+  const int64_t prefill_tiles =
+      ((int64_t)num_tokens * g + kPrefillPairs - 1) / kPrefillPairs + prefill_reqs;
   p.max_items = (int64_t)num_kv_heads * ((int64_t)num_reqs * p.max_splits + prefill_tiles);
   if (num_tokens == 0) p.max_items = 0;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };

@@ -14,6 +14,8 @@ constexpr int kPairsPerTile = 16;   // MFMA N width: (query row, q head) pairs p
 constexpr int kWaves = 4;           // waves per attention workgroup
 constexpr int kPrefillTilesPerWave = 2;  // 16-pair tiles one wave owns in a prefill item
 constexpr int kPrefillPairs = kWaves * kPrefillTilesPerWave * kPairsPerTile;  // 128
+constexpr int kPlanReqs = 1024;      // threads of the plan kernel; requests it ranks at once
+constexpr int kPlanMaxSplits = 2048; // partition counts the plan orders partition-major
 
 // Host-side plan of one attention call (derived from host scalars only).
 struct AttnPlan {

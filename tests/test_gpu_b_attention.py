@@ -95,6 +95,43 @@ def test_attention_forced_partitions(split_tokens):
     assert_attention_close(many, ref, wl.dtype, f"split {split_tokens}")
 
 
+def test_attention_many_requests():
+    """More requests than the work-list builder ranks at once (1024): the list
+    is built chunk by chunk in request order and must still cover every row."""
+    rng = np.random.default_rng(11)
+    R = 1500
+    nst = np.where(rng.random(R) < 0.9, 1, rng.integers(2, 9, R)).astype(np.int32)
+    nct = rng.integers(0, 200, R).astype(np.int32)
+    wl = workloads.build("many", nst, nct, num_q_heads=8, num_kv_heads=2, head_dim=64, seed=12,
+                         device=device())
+    _, _, _, out = gpu_step(wl)
+    _, _, _, ref = oracle_step(wl)
+    assert_attention_close(out, ref, wl.dtype, f"{R} requests")
+
+
+def test_attention_partitions_beyond_ordered_plan():
+    """More partitions per context (2063) than the work list orders partition-major
+    (2048): the request-order path runs and the reduce combines them all."""
+    wl = workloads.build("longsplit", [1, 1, 3], [66000, 40000, 10], num_q_heads=4,
+                         num_kv_heads=1, head_dim=64, seed=13, device=device())
+    _, _, _, out = gpu_step(wl, split_tokens=32)
+    _, _, _, ref = oracle_step(wl)
+    assert_attention_close(out, ref, wl.dtype, "2063 partitions")
+
+
+def test_attention_several_prompts_and_partitions():
+    """Several prompt chunks of different lengths next to decodes with different
+    partition counts, so the longest-first ordering reorders requests."""
+    nst = [1, 200, 1, 37, 1, 500, 1]
+    nct = [90, 10, 3000, 0, 700, 2500, 1500]
+    wl = workloads.build("order", nst, nct, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                         seed=14, device=device(), pool_slack=1.2)
+    _, _, _, ref = oracle_step(wl)
+    for st in (0, 256):
+        _, _, _, out = gpu_step(wl, split_tokens=st)
+        assert_attention_close(out, ref, wl.dtype, f"ordering, split {st}")
+
+
 def test_attention_block_permutation_invariance():
     """Moving physical blocks (and rewriting the table) leaves the GPU result
     bit-identical: the kernel's arithmetic order depends only on logical order."""
