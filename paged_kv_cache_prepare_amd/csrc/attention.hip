@@ -74,6 +74,16 @@ __device__ inline u32x2 keep_bf16x4(u32x2 v, unsigned keep) {
 
 __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// The block table is read-only for the whole call.  Reading it through the
+// constant address space lets wave-uniform lookups compile to scalar loads
+// (counted by lgkmcnt), so they never wait behind in-flight K/V vector loads,
+// also after a workgroup barrier.
+typedef const __attribute__((address_space(4))) int32_t table_t;
+
+__device__ inline table_t* table_row(const int32_t* block_table, int64_t row_stride, int r) {
+  return (table_t*)(block_table + (int64_t)r * row_stride);
+}
+
 // Rows of request r, or 0 when its query_start_loc range leaves [0, num_tokens)
 // (a broken precondition): such a request gets no work, so no kernel touches
 // rows outside q / out.
@@ -455,7 +465,7 @@ __device__ inline StepRsrc make_step(const AttnArgs& a, int b0, int b1, const ch
 template <int D, int NT>
 __device__ __attribute__((always_inline)) inline void walk_steps(
     TileState<D> (&st)[NT], const bf16x8 (&qf)[NT][Geometry<D>::KS], const int (&p_col)[NT],
-    const AttnArgs& a, const int32_t* __restrict__ bt, int nblk, int s_begin, int s_end,
+    const AttnArgs& a, table_t* bt, int nblk, int s_begin, int s_end,
     int p_unmasked, int seq_len, const char* kbase, const char* vbase, float c2) {
   if (s_begin >= s_end) return;
   const int lane = threadIdx.x & 63;
@@ -561,7 +571,7 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
   const int w_begin = sp_begin + wave * per_wave;
   const int w_end = min(sp_end, w_begin + per_wave);
 
-  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  table_t* bt = table_row(a.block_table, a.bt_stride, r);
   const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
 
@@ -745,26 +755,13 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   const int nsteps = p_hi_wg >= 0 ? min(ceil_div(L, kPrefillStep), p_hi_wg / kPrefillStep + 1)
                                    : 0;
 
-  const int32_t* __restrict__ bt = a.block_table + (int64_t)r * a.bt_stride;
+  table_t* bt = table_row(a.block_table, a.bt_stride, r);
   const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::kHeadBytes;
   const int nblk = L > 0 ? ceil_div(L, kBlock) : 0;
   const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
   const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
-
-  // validity of the 4 blocks of a step (bit b = block b is inside the context
-  // and its id lies in the pool); scalar loads, branch-free
-  auto step_valid = [&](int step) {
-    unsigned bits = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = 4 * step + b;
-      const int id = bt[min(j, last_col)];
-      bits |= (j < lim && id >= 0 && id < a.num_blocks) ? (1u << b) : 0u;
-    }
-    return bits;
-  };
 
   // lane-constant offsets of the staging loads and writes.  K load q of lane
   // (m = lane & 15, c = 4q + (lane >> 4)) moves dims 8c..8c+7 of token m; V
@@ -783,11 +780,20 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   }
   // this wave's fetch of block `wave` of a step into registers (a block past
   // the context or the walk gets a zero-count descriptor: no memory traffic)
+  // Returns the validity of the step's 4 blocks (bit b: block b lies inside the
+  // context and its id inside the pool), which every wave needs for masking.
   u32x4 rk[KQ], rv[KQ];
   auto fetch = [&](int step) {
-    const int j = 4 * step + wave;
-    const int id = bt[min(j, last_col)];
-    const bool ok = j < lim && step < nsteps && id >= 0 && id < a.num_blocks;
+    unsigned bits = 0;
+    int id = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = 4 * step + b;
+      const int idb = bt[min(j, last_col)];
+      bits |= (j < lim && step < nsteps && idb >= 0 && idb < a.num_blocks) ? (1u << b) : 0u;
+      id = (b == wave) ? idb : id;
+    }
+    const bool ok = (bits >> wave) & 1u;
     const int64_t off = (ok ? (int64_t)id : 0) * blk_stride;
     const rsrc_t rk_d = run_rsrc<D>(kbase + off, ok);
     const rsrc_t rv_d = run_rsrc<D>(vbase + off, ok);
@@ -796,6 +802,7 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
       rk[q] = __builtin_amdgcn_raw_buffer_load_b128(rk_d, k_src[q], 0, 0);
       rv[q] = __builtin_amdgcn_raw_buffer_load_b128(rv_d, v_src[q], 0, 0);
     }
+    return bits;
   };
   // write the fetched runs into LDS buffer `buf`; V tokens past the context are
   // zeroed here (their probability is 0, but the pool may hold NaN there)
@@ -829,16 +836,16 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
     mref[nt] = 0.f;
   }
 
-  fetch(0);
+  unsigned valid_next = fetch(0);
   stage(0, 0);
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    fetch(step + 1);
+    const unsigned valid = valid_next;
+    valid_next = fetch(step + 1);
     if (step * kPrefillStep <= p_hi) {
       const char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + k_rd;
       const char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + v_rd;
-      const unsigned valid = step_valid(step);
       const bool mask = (step * kPrefillStep + kPrefillStep - 1 > p_lo) || valid != 0xFu;
       // S^T = K Q^T for the 4 token tiles of the step
       f32x4 sacc[NT][4];
