@@ -2,7 +2,8 @@
 
 Every source under csrc/ is compiled to an object in parallel, then linked
 into ``paged_kv_cache_prepare_amd/libpkv.so``.  Packed-fp32 instructions are
-switched off for all device code (``-packed-fp32-ops``).
+switched off for all device code (``-packed-fp32-ops``).  ``FILE_FLAGS`` adds
+per-file options.
 """
 from __future__ import annotations
 
@@ -18,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 SOURCES = ["api.hip", "prepare.hip", "kv_write.hip", "attention.hip"]
+# Per-file flags.  The attention kernels never feed a NaN into a max or a sum
+# (masked scores are selected away first), so max operations need no NaN
+# canonicalisation.
+FILE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 
@@ -41,7 +46,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     def one(src):
         obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
-        cmd = [cc, *compile_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags([*FILE_FLAGS.get(src, []), *extra_flags]), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

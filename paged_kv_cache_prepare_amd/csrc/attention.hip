@@ -691,6 +691,7 @@ struct PrefillLayout {
 template <int D>
 struct PrefillSmem {
   char bytes[PrefillLayout<D>::total];
+  alignas(4) unsigned char valid[2][4];  // per buffer: block b of the step is readable
 };
 
 // Zero element e of an 8 x bf16 run when first + e >= limit.
@@ -780,20 +781,14 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   }
   // this wave's fetch of block `wave` of a step into registers (a block past
   // the context or the walk gets a zero-count descriptor: no memory traffic)
-  // Returns the validity of the step's 4 blocks (bit b: block b lies inside the
-  // context and its id inside the pool), which every wave needs for masking.
+  // This wave's fetch of block `wave` of a step into registers.  Returns whether
+  // the block is readable (inside the context, id inside the pool); a block
+  // that is not gets a zero-count descriptor and moves no memory.
   u32x4 rk[KQ], rv[KQ];
   auto fetch = [&](int step) {
-    unsigned bits = 0;
-    int id = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = 4 * step + b;
-      const int idb = bt[min(j, last_col)];
-      bits |= (j < lim && step < nsteps && idb >= 0 && idb < a.num_blocks) ? (1u << b) : 0u;
-      id = (b == wave) ? idb : id;
-    }
-    const bool ok = (bits >> wave) & 1u;
+    const int j = 4 * step + wave;
+    const int id = bt[min(j, last_col)];
+    const bool ok = j < lim && step < nsteps && id >= 0 && id < a.num_blocks;
     const int64_t off = (ok ? (int64_t)id : 0) * blk_stride;
     const rsrc_t rk_d = run_rsrc<D>(kbase + off, ok);
     const rsrc_t rv_d = run_rsrc<D>(vbase + off, ok);
@@ -802,13 +797,16 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
       rk[q] = __builtin_amdgcn_raw_buffer_load_b128(rk_d, k_src[q], 0, 0);
       rv[q] = __builtin_amdgcn_raw_buffer_load_b128(rv_d, v_src[q], 0, 0);
     }
-    return bits;
+    return ok;
   };
   // write the fetched runs into LDS buffer `buf`; V tokens past the context are
   // zeroed here (their probability is 0, but the pool may hold NaN there)
-  auto stage = [&](int step, int buf) {
+  // The validity flag goes to LDS too, so after the barrier every wave knows
+  // which of the step's 4 blocks hold keys.
+  auto stage = [&](int step, int buf, bool ok) {
     char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0);
     char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0);
+    if (lane == 0) sm.valid[buf][wave] = ok ? 1 : 0;
     const int tok0 = step * kPrefillStep + wave * kBlock;  // first token of this block
     const bool tail = tok0 + kBlock > L;
 #pragma unroll
@@ -836,16 +834,16 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
     mref[nt] = 0.f;
   }
 
-  unsigned valid_next = fetch(0);
-  stage(0, 0);
+  stage(0, 0, fetch(0));
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    const unsigned valid = valid_next;
-    valid_next = fetch(step + 1);
+    const bool ok_next = fetch(step + 1);
     if (step * kPrefillStep <= p_hi) {
       const char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + k_rd;
       const char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + v_rd;
+      const unsigned vw = *reinterpret_cast<const unsigned*>(sm.valid[buf]);
+      const unsigned valid = (vw & 1u) | ((vw >> 7) & 2u) | ((vw >> 14) & 4u) | ((vw >> 21) & 8u);
       const bool mask = (step * kPrefillStep + kPrefillStep - 1 > p_lo) || valid != 0xFu;
       // S^T = K Q^T for the 4 token tiles of the step
       f32x4 sacc[NT][4];
@@ -883,18 +881,24 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
             }
           }
         }
-        float mx = -INFINITY;
+        // This lane's max decides whether its column may need a new reference:
+        // the reference is column-uniform, so some lane of a column exceeds it
+        // exactly when the column max does.  Only then (rare after the first
+        // keys) are the column maxima formed with cross-lane shuffles.
+        float lmx = -INFINITY;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
-          mx = fmaxf(fmaxf(mx, fmaxf(sacc[nt][tt][0], sacc[nt][tt][1])),
-                     fmaxf(sacc[nt][tt][2], sacc[nt][tt][3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // the first key a column sees sets its reference; later ones move it
-        // only when the max grows by more than 2^kLazyLog2
-        const bool first = st[nt].m == -INFINITY && mx != -INFINITY;
-        const bool grow = first || mx * c2 > mref[nt] + kLazyLog2;
-        if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+          lmx = fmaxf(fmaxf(lmx, fmaxf(sacc[nt][tt][0], sacc[nt][tt][1])),
+                      fmaxf(sacc[nt][tt][2], sacc[nt][tt][3]));
+        const bool need = (st[nt].m == -INFINITY && lmx != -INFINITY) ||
+                          lmx * c2 > mref[nt] + kLazyLog2;
+        if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform
+          float mx = fmaxf(lmx, __shfl_xor(lmx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          // the first key a column sees sets its reference; later ones move it
+          // only when the max grows by more than 2^kLazyLog2
+          const bool first = st[nt].m == -INFINITY && mx != -INFINITY;
+          const bool grow = first || mx * c2 > mref[nt] + kLazyLog2;
           const float m_new = grow ? fmaxf(st[nt].m, mx) : st[nt].m;
           const float r_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
           const float alpha = (st[nt].m == -INFINITY) ? 0.f : fast_exp2(mref[nt] - r_new);
@@ -927,7 +931,7 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
         }
       }
     }
-    stage(step + 1, buf ^ 1);
+    stage(step + 1, buf ^ 1, ok_next);
     __syncthreads();
   }
 
