@@ -319,6 +319,13 @@ struct StepLoads {
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // Buffer descriptor word 3 for raw 32-bit buffer accesses on CDNA.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the decode K/V stream: non-temporal.  A decode item reads
+// each context block once (shared prefix blocks are read by a few concurrent
+// items at most), and the streaming policy sustains a markedly higher read
+// rate on scattered 4 KB runs.  Prefill tiles keep the default policy: every
+// tile of a prompt chunk re-reads the same blocks, which must stay cached.
+constexpr int kKvLoadPolicy = 2;
+constexpr int kPrefillLoadPolicy = 0;
 
 // Descriptor of one (block, kv head) run of a pool.  Its record count bounds
 // every access to that 16-token run in hardware; a masked block gets a count
@@ -339,13 +346,13 @@ __device__ inline void issue_step_loads(StepLoads<D>& ld, const StepRsrc& r, int
                                         int v_lane) {
 #pragma unroll
   for (int s = 0; s < Geometry<D>::KS; ++s) {
-    ld.k0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + s * 64, 0, 0));
-    ld.k1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + s * 64, 0, 0));
+    ld.k0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + s * 64, 0, kKvLoadPolicy));
+    ld.k1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + s * 64, 0, kKvLoadPolicy));
   }
 #pragma unroll
   for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
-    ld.v0[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v0, v_lane + dt * (16 * kBlock * 2), 0, 0);
-    ld.v1[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v1, v_lane + dt * (16 * kBlock * 2), 0, 0);
+    ld.v0[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v0, v_lane + dt * (16 * kBlock * 2), 0, kKvLoadPolicy);
+    ld.v1[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v1, v_lane + dt * (16 * kBlock * 2), 0, kKvLoadPolicy);
   }
 }
 
@@ -794,8 +801,8 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
     const rsrc_t rv_d = run_rsrc<D>(vbase + off, ok);
 #pragma unroll
     for (int q = 0; q < KQ; ++q) {
-      rk[q] = __builtin_amdgcn_raw_buffer_load_b128(rk_d, k_src[q], 0, 0);
-      rv[q] = __builtin_amdgcn_raw_buffer_load_b128(rv_d, v_src[q], 0, 0);
+      rk[q] = __builtin_amdgcn_raw_buffer_load_b128(rk_d, k_src[q], 0, kPrefillLoadPolicy);
+      rv[q] = __builtin_amdgcn_raw_buffer_load_b128(rv_d, v_src[q], 0, kPrefillLoadPolicy);
     }
     return ok;
   };
