@@ -74,6 +74,42 @@ __device__ inline u32x2 keep_bf16x4(u32x2 v, unsigned keep) {
 
 __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Max / sum over the four lanes n, n + 16, n + 32, n + 48 that hold one MFMA
+// column.  The row-swap permutes exchange 16-lane rows and 32-lane halves
+// between two copies of x; combining both copies gives every lane the
+// partner's value without an LDS round trip.  (The two results are copied
+// to scalars before any bit cast: bit-casting a subscript of the builtin's
+// result directly has been seen to read element 0 for both.)
+__device__ inline void swap_rows16(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+
+__device__ inline void swap_halves32(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+
+__device__ inline float column_max(float x) {
+  float a, b;
+  swap_rows16(x, a, b);
+  swap_halves32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+
+__device__ inline float column_sum(float x) {
+  float a, b;
+  swap_rows16(x, a, b);
+  swap_halves32(a + b, a, b);
+  return a + b;
+}
+
 // The block table is read-only for the whole call.  Reading it through the
 // constant address space lets wave-uniform lookups compile to scalar loads
 // (counted by lgkmcnt), so they never wait behind in-flight K/V vector loads,
@@ -394,8 +430,7 @@ __device__ inline void tile_step(TileState<D>& st, const bf16x8* qf, const StepL
   }
   float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                    fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = column_max(mx);
   const float m_new = fmaxf(st.m, mx);
   const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
   const float alpha = fast_exp2((st.m - m_use) * c2);
@@ -587,8 +622,7 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
   walk_steps<D, 1>(st, qf, p_col, a, bt, nblk, w_begin, w_end, L - q_len, L, kbase, vbase, c2);
 
   // merge the four waves' states
-  float l_tot = st[0].l + __shfl_xor(st[0].l, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = column_sum(st[0].l);
   if (g == 0) {
     sm.m[wave][n] = st[0].m;
     sm.l[wave][n] = l_tot;
@@ -688,8 +722,12 @@ constexpr float kLazyLog2 = 16.f;  // rescale when a column max grows by > 2^16
 
 template <int D>
 struct PrefillLayout {
-  static constexpr int kBytes = kPrefillStep * D * 2;  // one K buffer
-  static constexpr int vBytes = kPrefillStep * D * 2;  // one V buffer
+  // One run per block of the step.  K runs are 64 bytes apart modulo 256 so
+  // that the two blocks a K operand read touches fall in different banks.
+  static constexpr int kRun = kBlock * D * 2 + 64;
+  static constexpr int vRun = kBlock * D * 2;
+  static constexpr int kBytes = 4 * kRun;  // one K buffer
+  static constexpr int vBytes = 4 * vRun;  // one V buffer
   static constexpr int kOff0 = 0, kOff1 = kBytes;
   static constexpr int vOff0 = 2 * kBytes, vOff1 = 2 * kBytes + vBytes;
   static constexpr int total = 2 * kBytes + 2 * vBytes;
@@ -716,6 +754,156 @@ __device__ inline u32x4 keep_below(u32x4 v, int first, int limit) {
 template <typename T>
 __device__ inline T lds_ld(const char* base, int off) {
   return *reinterpret_cast<const T*>(base + off);
+}
+
+// S^T = K Q^T for the two 16-row tiles t = 0, 1 of half h of a 64-key step
+// (keys 32h..32h+31).  Rows are keys in a permuted order: row 4g + i of tile t
+// is key 8g + 4t + i of the half, so the 4 + 4 weights a lane (n, g) ends up
+// with are the 8 consecutive keys 8g..8g+7, all in block 2h + g / 2 -- one
+// contiguous 16-byte run of each V dim, and of the P^T B operand.
+template <int D, int NT>
+// Q arrives pre-scaled by scale * log2(e) and each column's accumulator starts
+// at -mref, so the result is already the log2 weight exponent of every key.
+__device__ __attribute__((always_inline)) inline void prefill_qk_half(
+    f32x4 (&s)[NT][2], const bf16x8 (&qf)[NT][Geometry<D>::KS], const char* kb, int h,
+    const float (&mref)[NT]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bf16x8 kf[Geometry<D>::KS];
+#pragma unroll
+    for (int k = 0; k < Geometry<D>::KS; ++k)
+      kf[k] = lds_ld<bf16x8>(kb, 2 * h * PrefillLayout<D>::kRun + 64 * t + 1024 * k);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 acc = {-mref[nt], -mref[nt], -mref[nt], -mref[nt]};
+#pragma unroll
+      for (int k = 0; k < Geometry<D>::KS; ++k) acc = mfma_bf16(kf[k], qf[nt][k], acc);
+      s[nt][t] = acc;
+    }
+  }
+}
+
+// Softmax weights of one half, P^T packed as the PV B operand: element j of
+// lane (n, g) is key 8g + j of the half (tile 0 gives j < 4, tile 1 the rest).
+// The scores are already log2 exponents relative to the column reference.
+template <int NT>
+__device__ __attribute__((always_inline)) inline void prefill_weights(bf16x8 (&p)[NT],
+                                                                      const f32x4 (&s)[NT][2]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[nt][i] = static_cast<__bf16>(fast_exp2(s[nt][0][i]));
+      p[nt][4 + i] = static_cast<__bf16>(fast_exp2(s[nt][1][i]));
+    }
+  }
+}
+
+// Mask, reference check and weights of one half.  Scores are held as
+//   x = scale * log2(e) * (q . k) - mref,
+// where mref is the column's reference max (log2 units).  The reference is
+// refreshed only when some column's max grows by more than 2^kLazyLog2, i.e.
+// some x exceeds kLazyLog2, or on the column's first key; then O and the
+// denominator are rescaled.  Otherwise the stale reference is kept and the
+// weights stay <= 2^kLazyLog2.  Numerator and denominator share the
+// reference, so the result is unchanged.  Each lane compares its own max;
+// the reference is column-uniform, so some lane of a column exceeds the bound
+// exactly when the column max does, and only then are column maxima formed
+// across lanes.  Weights are formed first and formed again in the rare refresh.
+// Scores of keys a column must not see become -inf: keys past its query
+// position, and every key of a block that holds no readable run.
+template <int NT>
+__device__ __attribute__((always_inline)) inline void prefill_mask_half(
+    f32x4 (&s)[NT][2], unsigned valid, int step, int h, const int (&p_col)[NT]) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const bool bok = (valid >> (2 * h + (g >> 1))) & 1u;
+  asm volatile("");  // keep the masked path a branch of its own
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kpos = step * kPrefillStep + 32 * h + 8 * g + 4 * t + i;
+        s[nt][t][i] = (bok && kpos <= p_col[nt]) ? s[nt][t][i] : -INFINITY;
+      }
+    }
+}
+
+// `later` holds scores of the step's other half formed with the same
+// reference; a refresh shifts them too.
+template <int D, int NT>
+__device__ __attribute__((always_inline)) inline void prefill_softmax_half(
+    bf16x8 (&p)[NT], f32x4 (&s)[NT][2], f32x4 (&later)[NT][2], f32x4 (&o)[NT][Geometry<D>::DT],
+    f32x4 (&lacc)[NT], float (&mref)[NT], bool (&has_ref)[NT]) {
+  float lmx[NT];
+  bool need = false;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    lmx[nt] = fmaxf(fmaxf(fmaxf(s[nt][0][0], s[nt][0][1]), fmaxf(s[nt][0][2], s[nt][0][3])),
+                    fmaxf(fmaxf(s[nt][1][0], s[nt][1][1]), fmaxf(s[nt][1][2], s[nt][1][3])));
+    need = need | (!has_ref[nt] & (lmx[nt] != -INFINITY)) | (lmx[nt] > kLazyLog2);
+  }
+  prefill_weights<NT>(p, s);
+  if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mx = column_max(lmx[nt]);
+      const bool first = !has_ref[nt] && mx != -INFINITY;
+      const bool grow = first || mx > kLazyLog2;
+      // a column without a reference has only seen masked keys: O and its
+      // denominator are still exactly 0
+      const float shift = grow ? mx : 0.f;
+      const float alpha = grow ? (has_ref[nt] ? fast_exp2(-mx) : 0.f) : 1.f;
+      lacc[nt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < Geometry<D>::DT; ++dt) o[nt][dt] *= alpha;
+      mref[nt] += shift;
+      has_ref[nt] = has_ref[nt] || first;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[nt][t] -= shift;
+        later[nt][t] -= shift;
+      }
+    }
+    prefill_weights<NT>(p, s);
+  }
+}
+
+// O^T += V^T P^T over keys 32h..32h+31, and the denominators (an all-ones A
+// operand sums exactly the bf16 weights the numerator uses).
+template <int D, int NT>
+__device__ __attribute__((always_inline)) inline void prefill_pv_half(
+    f32x4 (&o)[NT][Geometry<D>::DT], f32x4 (&lacc)[NT], const bf16x8 (&p)[NT], const char* vb,
+    int h, bf16x8 ones) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma_bf16(ones, p[nt], lacc[nt]);
+#pragma unroll
+  for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
+    const bf16x8 vf = lds_ld<bf16x8>(vb, 2 * h * PrefillLayout<D>::vRun + dt * 512);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma_bf16(vf, p[nt], o[nt][dt]);
+  }
+}
+
+// One 64-key step of a prefill tile from the staged K (kb) and V (vb) runs.
+// `mask` (wave-uniform) is set on the diagonal steps and on steps with an
+// unreadable block; only those pay for the per-key selects.
+template <int D, int NT>
+__device__ __attribute__((always_inline)) inline void prefill_step(
+    f32x4 (&o)[NT][Geometry<D>::DT], f32x4 (&lacc)[NT], float (&mref)[NT], bool (&has_ref)[NT],
+    const bf16x8 (&qf)[NT][Geometry<D>::KS], const char* kb, const char* vb, bool mask,
+    unsigned valid, int step, const int (&p_col)[NT], bf16x8 ones) {
+  f32x4 s0[NT][2], s1[NT][2];
+  bf16x8 p0[NT], p1[NT];
+  prefill_qk_half<D, NT>(s0, qf, kb, 0, mref);
+  if (mask) prefill_mask_half<NT>(s0, valid, step, 0, p_col);
+  prefill_qk_half<D, NT>(s1, qf, kb, 1, mref);
+  prefill_softmax_half<D, NT>(p0, s0, s1, o, lacc, mref, has_ref);
+  if (mask) prefill_mask_half<NT>(s1, valid, step, 1, p_col);
+  prefill_pv_half<D, NT>(o, lacc, p0, vb, 0, ones);
+  prefill_softmax_half<D, NT>(p1, s1, s0, o, lacc, mref, has_ref);
+  prefill_pv_half<D, NT>(o, lacc, p1, vb, 1, ones);
 }
 
 template <int D>
@@ -749,8 +937,14 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
                        ((int64_t)(row0 + t) * a.q_stride + (int64_t)head * D) * 2;
 #pragma unroll
     for (int s = 0; s < Geo::KS; ++s) {
-      qf[nt][s] = ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
-                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      bf16x8 v = ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
+                    : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      // scores come out in log2 units: Q carries scale * log2(e), rounded
+      // once to bf16 (2^-9 relative per element, well below the bf16
+      // rounding of the weights)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(static_cast<float>(v[e]) * c2);
+      qf[nt][s] = v;
     }
   }
   // rows seen by this wave and by the whole workgroup
@@ -771,174 +965,113 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
   const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
 
-  // lane-constant offsets of the staging loads and writes.  K load q of lane
-  // (m = lane & 15, c = 4q + (lane >> 4)) moves dims 8c..8c+7 of token m; V
-  // load q moves tokens 8h..8h+7 of dim 16*dt + (lane & 15), where
-  // 2*dt + h = 4q + (lane >> 4), and is written as two 8-byte halves.
-  int k_src[KQ], k_st[KQ], v_src[KQ], v_st[KQ], v_half[KQ];
-#pragma unroll
-  for (int q = 0; q < KQ; ++q) {
-    const int m = lane & 15, c = 4 * q + (lane >> 4);
-    k_src[q] = m * 2 * D + 16 * c;
-    k_st[q] = ((wave * (D / 8) + c) * 16 + m) * 16;
-    const int grp = 4 * q + (lane >> 4), dt = grp >> 1, h = grp & 1;
-    v_src[q] = (16 * dt + (lane & 15)) * 2 * kBlock + 16 * h;
-    v_st[q] = (((wave >> 1) * (D / 16) + dt) * 4 + 2 * h) * 256 + (lane & 15) * 16 + 8 * (wave & 1);
-    v_half[q] = h;
-  }
-  // this wave's fetch of block `wave` of a step into registers (a block past
-  // the context or the walk gets a zero-count descriptor: no memory traffic)
-  // This wave's fetch of block `wave` of a step into registers.  Returns whether
-  // the block is readable (inside the context, id inside the pool); a block
-  // that is not gets a zero-count descriptor and moves no memory.
-  u32x4 rk[KQ], rv[KQ];
-  auto fetch = [&](int step) {
+  // LDS layout of one buffer: a K area and a V area, each with one run per
+  // block of the step (block b is the one wave b fetches), copied straight
+  // from the pools by LDS-direct buffer loads (lane i of a load fills bytes
+  // 16i..16i+15 of its 1 KB destination).
+  //   K run: 1 KB per k-step s; lane (m = i & 15, gg = i >> 4) holds dims
+  //          8(4s + gg)..+7 of token m, the MFMA A-operand order.
+  //   V run: chunk (dim, c) = tokens 8c..8c+7 of one dim, at 16-byte slot
+  //          (dim / 16) * 32 + c * 16 + dim % 16, so the 4-token runs that
+  //          form a PV operand are read 8 bytes per lane, conflict-free.
+  // Source offsets of copy q: K token (lane & 15), dims 8(4q + (lane >> 4));
+  // V slot q * 64 + lane.  Both are a lane base plus q times a constant.
+  const int k_src = (lane & 15) * 2 * D + 16 * (lane >> 4);            // + 64 q
+  const int v_src = ((lane >> 5) * 16 + (lane & 15)) * 2 * kBlock +     // + 1024 q
+                    16 * ((lane >> 4) & 1);
+  typedef __attribute__((address_space(3))) void lds_void;
+  // Issue this wave's copy of block `wave` of a step into LDS buffer `buf`.
+  // Returns whether the block is readable (inside the context, id inside the
+  // pool); a block that is not is not read at all.
+  auto fetch = [&](int step, int buf) {
     const int j = 4 * step + wave;
     const int id = bt[min(j, last_col)];
     const bool ok = j < lim && step < nsteps && id >= 0 && id < a.num_blocks;
-    const int64_t off = (ok ? (int64_t)id : 0) * blk_stride;
-    const rsrc_t rk_d = run_rsrc<D>(kbase + off, ok);
-    const rsrc_t rv_d = run_rsrc<D>(vbase + off, ok);
+    if (ok) {
+      const int64_t off = (int64_t)id * blk_stride;
+      const rsrc_t rk_d = run_rsrc<D>(kbase + off, true);
+      const rsrc_t rv_d = run_rsrc<D>(vbase + off, true);
+      char* kdst = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + wave * Lay::kRun;
+      char* vdst = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + wave * Lay::vRun;
 #pragma unroll
-    for (int q = 0; q < KQ; ++q) {
-      rk[q] = __builtin_amdgcn_raw_buffer_load_b128(rk_d, k_src[q], 0, kPrefillLoadPolicy);
-      rv[q] = __builtin_amdgcn_raw_buffer_load_b128(rv_d, v_src[q], 0, kPrefillLoadPolicy);
+      for (int q = 0; q < KQ; ++q) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_d, (lds_void*)(kdst + q * 1024), 16,
+                                                 k_src + 64 * q, 0, 0, kPrefillLoadPolicy);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_d, (lds_void*)(vdst + q * 1024), 16,
+                                                 v_src + 1024 * q, 0, 0, kPrefillLoadPolicy);
+      }
     }
     return ok;
   };
-  // write the fetched runs into LDS buffer `buf`; V tokens past the context are
-  // zeroed here (their probability is 0, but the pool may hold NaN there)
-  // The validity flag goes to LDS too, so after the barrier every wave knows
-  // which of the step's 4 blocks hold keys.
-  auto stage = [&](int step, int buf, bool ok) {
-    char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0);
-    char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0);
+  // After this wave's copies have landed: publish the block's validity (every
+  // wave needs it for masking), zero the V run of a block that was not read,
+  // and zero V tokens past the context in the last block (their weight is 0,
+  // but the pool may hold NaN there and 0 * NaN would poison the sum).
+  auto finish = [&](int step, int buf, bool ok) {
+    char* vdst = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + wave * Lay::vRun;
     if (lane == 0) sm.valid[buf][wave] = ok ? 1 : 0;
     const int tok0 = step * kPrefillStep + wave * kBlock;  // first token of this block
-    const bool tail = tok0 + kBlock > L;
+    if (!ok) {
 #pragma unroll
-    for (int q = 0; q < KQ; ++q) {
-      *reinterpret_cast<u32x4*>(kb + k_st[q]) = rk[q];
-      u32x4 v = rv[q];
-      if (tail) v = keep_below(v, tok0 + 8 * v_half[q], L);
-      *reinterpret_cast<u32x2*>(vb + v_st[q]) = u32x2{v.x, v.y};
-      *reinterpret_cast<u32x2*>(vb + v_st[q] + 256) = u32x2{v.z, v.w};
+      for (int q = 0; q < KQ; ++q)
+        *reinterpret_cast<u32x4*>(vdst + q * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+    } else if (tok0 + kBlock > L) {
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        u32x4* pv = reinterpret_cast<u32x4*>(vdst + q * 1024 + 16 * lane);
+        *pv = keep_below(*pv, tok0 + 8 * (((q * 64 + lane) >> 4) & 1), L);
+      }
     }
   };
+  // vmcnt(0): the LDS-direct copies are not tracked by the compiler's own
+  // waits, so each wave waits for its copies before the workgroup barrier.
+  auto wait_copies = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
   // lane-constant LDS offsets of the MFMA operand reads
-  const int k_rd = 16 * lane;  // + immediates for tile / k-step
-  const int v_rd = 16 * lane;  // + immediates for k-step / dim tile
+  // K operand row n of tile 0 is key 8(n / 4) + n % 4 of the half: block
+  // n / 8 of the half, token 8((n / 4) % 2) + n % 4; lane (n, g) reads dims
+  // 8(4k + g)..+7 of it.  V operand lane (n, g) reads dim 16 dt + n, keys
+  // 8(g % 2)..+7 of block g / 2 of the half.
+  const int k_rd = (n >> 3) * Lay::kRun + (g * 16 + 8 * ((n >> 2) & 1) + (n & 3)) * 16;
+  const int v_rd = (g >> 1) * Lay::vRun + ((g & 1) * 16 + n) * 16;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
                                                        0x3F803F80u});
 
-  TileState<D> st[NT];
-  f32x4 lacc[NT];   // softmax denominators (every row of a column holds the same sum)
-  float mref[NT];   // m * c2 of the reference max, 0 while a column has no key yet
+  f32x4 o[NT][Geo::DT];  // O^T: lane (n, g) holds dims 16*dt + 4*g + i of column n
+  f32x4 lacc[NT];        // softmax denominators (every row of a column holds the same sum)
+  float mref[NT];        // reference max of the column in log2 units (0 until its first key)
+  bool has_ref[NT];      // the column has seen a visible key
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    tile_init(st[nt]);
+#pragma unroll
+    for (int dt = 0; dt < Geo::DT; ++dt) o[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     mref[nt] = 0.f;
+    has_ref[nt] = false;
   }
 
-  stage(0, 0, fetch(0));
+  {
+    const bool ok0 = fetch(0, 0);
+    wait_copies();
+    finish(0, 0, ok0);
+  }
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    const bool ok_next = fetch(step + 1);
+    const bool ok_next = fetch(step + 1, buf ^ 1);
     if (step * kPrefillStep <= p_hi) {
       const char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + k_rd;
       const char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + v_rd;
       const unsigned vw = *reinterpret_cast<const unsigned*>(sm.valid[buf]);
       const unsigned valid = (vw & 1u) | ((vw >> 7) & 2u) | ((vw >> 14) & 4u) | ((vw >> 21) & 8u);
       const bool mask = (step * kPrefillStep + kPrefillStep - 1 > p_lo) || valid != 0xFu;
-      // S^T = K Q^T for the 4 token tiles of the step
-      f32x4 sacc[NT][4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        bf16x8 kf[Geo::KS];
-#pragma unroll
-        for (int s = 0; s < Geo::KS; ++s)
-          kf[s] = lds_ld<bf16x8>(kb, (tt * (D / 8) + 4 * s) * 256);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < Geo::KS; ++s) acc = mfma_bf16(kf[s], qf[nt][s], acc);
-          sacc[nt][tt] = acc;
-        }
-      }
-      // softmax weights, P^T packed for the PV MFMA.  The reference max is
-      // refreshed only when some column's max grows by more than 2^kLazyLog2
-      // (then O and the denominator are rescaled); otherwise the stale
-      // reference is kept and the weights stay <= 2^kLazyLog2.  Numerator and
-      // denominator share the reference, so the result is unchanged.
-      bf16x8 pf[NT][2];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (mask) {
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const int tok = 16 * tt + 4 * g;  // + i
-            const bool bok = (valid >> tt) & 1u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kpos = step * kPrefillStep + tok + i;
-              sacc[nt][tt][i] = (bok && kpos <= p_col[nt]) ? sacc[nt][tt][i] : -INFINITY;
-            }
-          }
-        }
-        // This lane's max decides whether its column may need a new reference:
-        // the reference is column-uniform, so some lane of a column exceeds it
-        // exactly when the column max does.  Only then (rare after the first
-        // keys) are the column maxima formed with cross-lane shuffles.
-        float lmx = -INFINITY;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          lmx = fmaxf(fmaxf(lmx, fmaxf(sacc[nt][tt][0], sacc[nt][tt][1])),
-                      fmaxf(sacc[nt][tt][2], sacc[nt][tt][3]));
-        const bool need = (st[nt].m == -INFINITY && lmx != -INFINITY) ||
-                          lmx * c2 > mref[nt] + kLazyLog2;
-        if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform
-          float mx = fmaxf(lmx, __shfl_xor(lmx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          // the first key a column sees sets its reference; later ones move it
-          // only when the max grows by more than 2^kLazyLog2
-          const bool first = st[nt].m == -INFINITY && mx != -INFINITY;
-          const bool grow = first || mx * c2 > mref[nt] + kLazyLog2;
-          const float m_new = grow ? fmaxf(st[nt].m, mx) : st[nt].m;
-          const float r_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
-          const float alpha = (st[nt].m == -INFINITY) ? 0.f : fast_exp2(mref[nt] - r_new);
-          lacc[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < Geo::DT; ++dt) st[nt].o[dt] *= alpha;
-          st[nt].m = m_new;
-          mref[nt] = r_new;
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pf[nt][kk][i] = static_cast<__bf16>(fast_exp2(fmaf(sacc[nt][2 * kk][i], c2, -mref[nt])));
-            pf[nt][kk][4 + i] =
-                static_cast<__bf16>(fast_exp2(fmaf(sacc[nt][2 * kk + 1][i], c2, -mref[nt])));
-          }
-        }
-      }
-      // O^T += V^T P^T, and the denominators
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma_bf16(ones, pf[nt][kk], lacc[nt]);
-#pragma unroll
-        for (int dt = 0; dt < Geo::DT; ++dt) {
-          const bf16x8 vf = lds_ld<bf16x8>(vb, (kk * (D / 16) + dt) * 4 * 256);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) st[nt].o[dt] = mfma_bf16(vf, pf[nt][kk], st[nt].o[dt]);
-        }
-      }
+      // The step runs as two 32-key halves in a software pipeline: the QK
+      // MFMAs of half 1 are issued next to the softmax of half 0, and the PV
+      // MFMAs of half 0 next to the softmax of half 1, so each wave keeps its
+      // matrix unit busy while its vector unit forms the weights.
+      prefill_step<D, NT>(o, lacc, mref, has_ref, qf, kb, vb, mask, valid, step, p_col, ones);
     }
-    stage(step + 1, buf ^ 1, ok_next);
+    wait_copies();
+    finish(step + 1, buf ^ 1, ok_next);
     __syncthreads();
   }
 
@@ -955,9 +1088,9 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
                   ((int64_t)(row0 + t) * a.out_stride + (int64_t)head * D + 4 * g) * 2;
 #pragma unroll
       for (int dt = 0; dt < Geo::DT; ++dt) {
-        const f32x4 o = st[nt].o[dt];
-        u16x4 b = {bf16_bits(o[0] * inv), bf16_bits(o[1] * inv), bf16_bits(o[2] * inv),
-                   bf16_bits(o[3] * inv)};
+        const f32x4 v = o[nt][dt];
+        u16x4 b = {bf16_bits(v[0] * inv), bf16_bits(v[1] * inv), bf16_bits(v[2] * inv),
+                   bf16_bits(v[3] * inv)};
         *reinterpret_cast<u16x4*>(dst + dt * 32) = b;
       }
     }
