@@ -896,14 +896,21 @@ __device__ __attribute__((always_inline)) inline void prefill_step(
     unsigned valid, int step, const int (&p_col)[NT], bf16x8 ones) {
   f32x4 s0[NT][2], s1[NT][2];
   bf16x8 p0[NT], p1[NT];
+  // The two MFMA-only stretches (QK of half 0, PV of half 1) run at raised
+  // wave priority, so the SIMD's other wave gets the issue slots for its
+  // vector work while this one keeps the matrix unit fed.
+  __builtin_amdgcn_s_setprio(1);
   prefill_qk_half<D, NT>(s0, qf, kb, 0, mref);
+  __builtin_amdgcn_s_setprio(0);
   if (mask) prefill_mask_half<NT>(s0, valid, step, 0, p_col);
   prefill_qk_half<D, NT>(s1, qf, kb, 1, mref);
   prefill_softmax_half<D, NT>(p0, s0, s1, o, lacc, mref, has_ref);
   if (mask) prefill_mask_half<NT>(s1, valid, step, 1, p_col);
   prefill_pv_half<D, NT>(o, lacc, p0, vb, 0, ones);
   prefill_softmax_half<D, NT>(p1, s1, s0, o, lacc, mref, has_ref);
+  __builtin_amdgcn_s_setprio(1);
   prefill_pv_half<D, NT>(o, lacc, p1, vb, 1, ones);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D>
