@@ -870,19 +870,27 @@ __device__ __attribute__((always_inline)) inline void prefill_softmax_half(
   }
 }
 
+// V^T operands of half h, one per 16-dim tile.  They are read from LDS
+// before the half's softmax, so their latency hides behind the exponentials.
+template <int D>
+__device__ __attribute__((always_inline)) inline void prefill_v_read(
+    bf16x8 (&vf)[Geometry<D>::DT], const char* vb, int h) {
+#pragma unroll
+  for (int dt = 0; dt < Geometry<D>::DT; ++dt)
+    vf[dt] = lds_ld<bf16x8>(vb, 2 * h * PrefillLayout<D>::vRun + dt * 512);
+}
 // O^T += V^T P^T over keys 32h..32h+31, and the denominators (an all-ones A
 // operand sums exactly the bf16 weights the numerator uses).
 template <int D, int NT>
 __device__ __attribute__((always_inline)) inline void prefill_pv_half(
-    f32x4 (&o)[NT][Geometry<D>::DT], f32x4 (&lacc)[NT], const bf16x8 (&p)[NT], const char* vb,
-    int h, bf16x8 ones) {
+    f32x4 (&o)[NT][Geometry<D>::DT], f32x4 (&lacc)[NT], const bf16x8 (&p)[NT],
+    const bf16x8 (&vf)[Geometry<D>::DT], bf16x8 ones) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma_bf16(ones, p[nt], lacc[nt]);
 #pragma unroll
   for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
-    const bf16x8 vf = lds_ld<bf16x8>(vb, 2 * h * PrefillLayout<D>::vRun + dt * 512);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma_bf16(vf, p[nt], o[nt][dt]);
+    for (int nt = 0; nt < NT; ++nt) o[nt][dt] = mfma_bf16(vf[dt], p[nt], o[nt][dt]);
   }
 }
 
@@ -904,12 +912,15 @@ __device__ __attribute__((always_inline)) inline void prefill_step(
   __builtin_amdgcn_s_setprio(0);
   if (mask) prefill_mask_half<NT>(s0, valid, step, 0, p_col);
   prefill_qk_half<D, NT>(s1, qf, kb, 1, mref);
+  bf16x8 vf[Geometry<D>::DT];
+  prefill_v_read<D>(vf, vb, 0);
   prefill_softmax_half<D, NT>(p0, s0, s1, o, lacc, mref, has_ref);
   if (mask) prefill_mask_half<NT>(s1, valid, step, 1, p_col);
-  prefill_pv_half<D, NT>(o, lacc, p0, vb, 0, ones);
+  prefill_pv_half<D, NT>(o, lacc, p0, vf, ones);
+  prefill_v_read<D>(vf, vb, 1);
   prefill_softmax_half<D, NT>(p1, s1, s0, o, lacc, mref, has_ref);
   __builtin_amdgcn_s_setprio(1);
-  prefill_pv_half<D, NT>(o, lacc, p1, vb, 1, ones);
+  prefill_pv_half<D, NT>(o, lacc, p1, vf, ones);
   __builtin_amdgcn_s_setprio(0);
 }
 
