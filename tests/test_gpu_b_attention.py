@@ -205,3 +205,49 @@ def test_attention_strided_q_and_out():
     torch.cuda.synchronize()
     assert torch.equal(bits_view(ov.contiguous()), bits_view(ref_out))
     assert (big[:, :128] == 7).all() and (big[:, 9 * 128:] == 7).all()
+
+
+# Shared-prefix groups: single-token decodes whose first logical blocks are the
+# same physical blocks are computed together over the partitions they share.
+# (Hq, Hkv, d, nst, nct, groups [(members, prefix tokens)], split_tokens)
+SHARED = [
+    # G=8: a group of 5 (an item of 4 + a lone member), a group of 2 with a
+    # prefix that ends inside a partition, unshared decodes, a prompt chunk and
+    # a two-row decode that shares blocks but is not grouped
+    (32, 4, 128, [1, 1, 1, 1, 1, 1, 1, 40, 1, 2],
+     [1500, 2000, 1100, 3000, 1030, 700, 900, 1200, 520, 1400],
+     [([0, 1, 2, 3, 4, 9], 1024), ([6, 8], 496)], (64, 256, 0)),
+    # G=1: 40 members, items of 32 + 8
+    (8, 8, 128, [1] * 44, [300 + 7 * i for i in range(44)],
+     [(list(range(40)), 256)], (64, 0)),
+    # G=16 (one kv head), head_dim 64: items of 2 + 1
+    (16, 1, 64, [1, 1, 1, 1], [800, 650, 1200, 90], [([0, 1, 2], 512)], (32, 128)),
+    # G=4, head_dim 64, two groups side by side
+    (16, 4, 64, [1] * 7, [400, 410, 420, 430, 600, 610, 50],
+     [([0, 1, 2, 3], 384), ([4, 5], 592)], (96, 0)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SHARED)))
+def test_attention_shared_prefix_groups(case):
+    Hq, Hkv, d, nst, nct, groups, splits = SHARED[case]
+    wl = workloads.build(f"shared{case}", nst, nct, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                         seed=90 + case, device=device(), pool_slack=1.2,
+                         shared_prefix_groups=groups)
+    _, _, _, ref = oracle_step(wl)
+    for st in splits:
+        _, _, _, out = gpu_step(wl, split_tokens=st)
+        assert_attention_close(out, ref, wl.dtype, f"shared{case} split {st}")
+
+
+def test_attention_prefix_that_diverges_and_rejoins():
+    """Two decodes whose tables agree on blocks 0-5 and 7 but not 6: only the
+    partitions before block 6 may be computed once for both."""
+    wl = workloads.build("diverge", [1, 1, 1], [700, 650, 300], num_q_heads=16, num_kv_heads=2,
+                         head_dim=128, seed=31, device=device(), pool_slack=1.0)
+    wl.block_table[1, :6] = wl.block_table[0, :6]
+    wl.block_table[1, 7] = wl.block_table[0, 7]
+    _, _, _, ref = oracle_step(wl)
+    for st in (32, 64, 128):
+        _, _, _, out = gpu_step(wl, split_tokens=st)
+        assert_attention_close(out, ref, wl.dtype, f"diverging prefix, split {st}")
