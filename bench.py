@@ -50,6 +50,9 @@ def parse():
                    help="context partition size of decode items (0 = library default)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate budget of the CPU oracle baseline")
+    p.add_argument("--graph", action="store_true",
+                   help="also capture the step in a HIP graph and time K replays; value and "
+                        "ms_per_step then come from the replays")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="instead of the step, time a plain device-to-device copy of this many "
                         "MiB (the known-size kernel that HBM byte counters are scaled by)")
@@ -263,6 +266,27 @@ def main():
                    for e in events])
     t_prep, t_write, t_attn = (float(np.mean(ph[:, i])) for i in range(3))
 
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        eager_ms, ms_step = ms_step, graph_ms
+
     attn_s = t_attn / 1e3
     flops = work["flops_decode"] + work["flops_prefill"]
     gbs = work["bytes_unique"] / attn_s / 1e9
@@ -307,6 +331,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if graph_ms is not None:
+        line["graph"] = {"ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(eager_ms, 4),
+                         "note": "value and ms_per_step come from HIP-graph replays of the step"}
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,101 @@
+"""A whole step (prepare -> kv write -> attention) captured in a HIP graph and
+replayed: every replay must reproduce the eager result bit for bit, also after
+the inputs are rewritten in place between replays ("How vLLM Works
+Internally: A Deep Dive", "CUDA Graphs": a fixed-shape step is recorded once
+and replayed).  The library allocates nothing and clears nothing with memset,
+so the step is capturable as is."""
+import pytest
+import torch
+
+import paged_kv_cache_prepare_amd as pkv
+from paged_kv_cache_prepare_amd import workloads
+
+from gpu_helpers import bits_view, device, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _buffers(wl, dev):
+    T, R = wl.num_tokens, wl.num_reqs
+    i32 = dict(dtype=torch.int32, device=dev)
+    prep = {"req_indices": torch.empty(T, **i32), "positions": torch.empty(T, **i32),
+            "slot_mapping": torch.empty(T, dtype=torch.int64, device=dev),
+            "query_start_loc": torch.empty(R + 1, **i32), "seq_lens": torch.empty(R, **i32),
+            "logits_indices": torch.empty(R, **i32)}
+    ws = torch.empty(max(256, pkv.attention_workspace_bytes(
+        R, T, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.max_query_len, wl.max_seq_len, 64,
+        wl.dtype)), dtype=torch.uint8, device=dev)
+    return prep, ws
+
+
+def test_step_replays_in_a_hip_graph():
+    dev = device()
+    # decodes that are split into partitions, a prompt chunk, a short multi-row decode
+    wl = workloads.build("graph", [1, 1, 70, 3, 1], [900, 40, 100, 20, 2000], num_q_heads=16,
+                         num_kv_heads=4, head_dim=128, seed=23, device=dev, pool_slack=1.2)
+    nst = torch.from_numpy(wl.num_scheduled_tokens).to(dev)
+    nct = torch.from_numpy(wl.num_computed_tokens).to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    q, key, value = wl.q.clone(), wl.key.clone(), wl.value.clone()
+    kc0, vc0 = wl.key_cache.clone(), wl.value_cache.clone()
+    kc, vc = kc0.clone(), vc0.clone()
+    out = torch.empty_like(q)
+    prep, ws = _buffers(wl, dev)
+
+    def step():
+        pkv.prepare_inputs(nst, nct, bt, num_tokens=wl.num_tokens, block_size=wl.block_size,
+                           num_blocks=wl.num_blocks, out=prep)
+        pkv.kv_cache_write(key, value, kc, vc, prep["slot_mapping"], block_size=wl.block_size)
+        pkv.paged_attention(q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                            scale=wl.scale, out=out, split_tokens=64, workspace=ws)
+
+    def eager_reference():
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        step()
+        torch.cuda.synchronize()
+        return ({k: v.clone() for k, v in prep.items()}, kc.clone(), vc.clone(), out.clone())
+
+    ref = eager_reference()
+    # capture (torch warms up on a side stream first)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    kc.copy_(kc0)
+    vc.copy_(vc0)
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    for rep in range(6):
+        if rep == 3:  # new activations of the same shapes, written in place
+            q.copy_(torch.randn(q.shape, generator=gen, device=dev).to(q.dtype))
+            key.copy_(torch.randn(key.shape, generator=gen, device=dev).to(key.dtype))
+            value.copy_(torch.randn(value.shape, generator=gen, device=dev).to(value.dtype))
+            ref = eager_reference()
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        out.fill_(float("nan"))
+        for v in prep.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        rp, rk, rv, ro = ref
+        for k in rp:
+            assert torch.equal(prep[k], rp[k]), f"replay {rep}: {k}"
+        assert torch.equal(bits_view(kc), bits_view(rk)), f"replay {rep}: K pool"
+        assert torch.equal(bits_view(vc), bits_view(rv)), f"replay {rep}: V pool"
+        assert torch.equal(bits_view(out), bits_view(ro)), f"replay {rep}: attention output"
+        log(f"  replay {rep}: bit-identical to the eager step")
+        # eager work between replays on the same stream
+        eager_reference()
