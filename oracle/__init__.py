@@ -43,6 +43,7 @@ ERR_NOMEM = 5
 
 F32 = 0
 BF16 = 1
+FP8 = 2
 
 
 class OracleError(RuntimeError):
@@ -83,6 +84,16 @@ def _load():
     lib.orc_attention.argtypes = [P, i64, P, P, i32, P, P, P, i64, i32, i32, i32, i32, i32,
                                   i32, i64, f64, P, i32, P, i32]
     lib.orc_attention.restype = ctypes.c_int
+    lib.orc_attention_kv.argtypes = [P, i64, P, P, i32, i32, f64, f64, P, P, P, i64, i32, i32,
+                                     i32, i32, i32, i32, i64, f64, P, i32, P, i32]
+    lib.orc_attention_kv.restype = ctypes.c_int
+    lib.orc_kv_write_fp8.argtypes = [P, P, i64, i64, P, P, i64, P, i32, i32, i32, i32, i32,
+                                     ctypes.c_float, ctypes.c_float]
+    lib.orc_kv_write_fp8.restype = ctypes.c_int
+    lib.orc_fp8_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_fp8_decode.restype = f64
+    lib.orc_fp8_encode.argtypes = [ctypes.c_float]
+    lib.orc_fp8_encode.restype = ctypes.c_uint8
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -155,11 +166,44 @@ def kv_write(key, value, key_cache, value_cache, slot_mapping, block_size: int) 
         raise OracleError(rc, "kv_write")
 
 
+def fp8_decode(code: int) -> float:
+    """Value of one FP8 E4M3 code; see ``orc_fp8_decode``."""
+    return float(_load().orc_fp8_decode(int(code)))
+
+
+def fp8_encode(x: float) -> int:
+    """E4M3 code of a binary32 value (nearest, ties to even, saturating); see
+    ``orc_fp8_encode``."""
+    return int(_load().orc_fp8_encode(float(np.float32(x))))
+
+
+def kv_write_fp8(key, value, key_cache, value_cache, slot_mapping, block_size: int,
+                 k_scale: float, v_scale: float) -> None:
+    """FP8 form of :func:`kv_write`; see ``orc_kv_write_fp8``.
+
+    ``key``/``value`` are [T, Hkv, d] bf16 or fp32; the pools are uint8 arrays or
+    tensors with [nb, Hkv, bs, d] (K) and [nb, Hkv, d * bs] (V, the FP8 layout)
+    bytes; the scales are binary32 values.
+    """
+    T, H, d = key.shape
+    nb = key_cache.shape[0]
+    slots = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64))
+    esz = key.element_size() if hasattr(key, "element_size") else key.itemsize
+    rc = _load().orc_kv_write_fp8(_ptr(key), _ptr(value), H * d, H * d, _ptr(key_cache),
+                                  _ptr(value_cache), nb, _ptr(slots), T, H, d, block_size, esz,
+                                  float(np.float32(k_scale)), float(np.float32(v_scale)))
+    if rc != OK:
+        raise OracleError(rc, "kv_write_fp8")
+
+
 def attention(q, key_cache, value_cache, query_start_loc, seq_lens, block_table,
-              block_size: int, scale: float, rows=None, num_threads: int = 0) -> np.ndarray:
-    """fp64 causal paged attention; see ``orc_attention``.
+              block_size: int, scale: float, rows=None, num_threads: int = 0,
+              kv_scales=None) -> np.ndarray:
+    """fp64 causal paged attention; see ``orc_attention`` / ``orc_attention_kv``.
 
     ``q`` is [T, Hq, d] (fp32 or bf16 CPU tensor, or float32 numpy array).
+    With ``kv_scales = (k_scale, v_scale)`` the pools hold FP8 E4M3 bytes
+    (uint8) in the FP8 layouts and every element reads as code value x scale.
     Returns a float64 array [len(rows), Hq, d] (all T rows when ``rows`` is None).
     """
     T, Hq, d = q.shape
@@ -170,7 +214,12 @@ def attention(q, key_cache, value_cache, query_start_loc, seq_lens, block_table,
     else:
         import torch
         dtype = {torch.float32: F32, torch.bfloat16: BF16}[q.dtype]
-        assert key_cache.dtype == q.dtype and value_cache.dtype == q.dtype
+        if kv_scales is None:
+            assert key_cache.dtype == q.dtype and value_cache.dtype == q.dtype
+    kv_dtype, ks, vs = dtype, 1.0, 1.0
+    if kv_scales is not None:
+        kv_dtype = FP8
+        ks, vs = (float(np.float32(x)) for x in kv_scales)
     qsl = _i32(query_start_loc)
     sl = _i32(seq_lens)
     R = int(sl.shape[0])
@@ -182,10 +231,10 @@ def attention(q, key_cache, value_cache, query_start_loc, seq_lens, block_table,
         sel = _i32(rows)
         n = int(sel.shape[0])
     out = np.zeros((n, Hq, d), np.float64)
-    rc = _load().orc_attention(
-        _ptr(q), Hq * d, _ptr(key_cache), _ptr(value_cache), dtype, _ptr(qsl), _ptr(sl),
-        _ptr(bt), bt.shape[1], bt.shape[1], R, Hq, Hkv, d, block_size, nb, float(scale),
-        _ptr(sel), n, _ptr(out), int(num_threads))
+    rc = _load().orc_attention_kv(
+        _ptr(q), Hq * d, _ptr(key_cache), _ptr(value_cache), dtype, kv_dtype, ks, vs, _ptr(qsl),
+        _ptr(sl), _ptr(bt), bt.shape[1], bt.shape[1], R, Hq, Hkv, d, block_size, nb,
+        float(scale), _ptr(sel), n, _ptr(out), int(num_threads))
     if rc != OK:
         raise OracleError(rc, "attention")
     return out

@@ -22,6 +22,13 @@
  *                     softmax attention in fp64 ("How vLLM Works Internally:
  *                     A Deep Dive", "How the Kernel Works", its four steps;
  *                     "Inside vLLM...", Part 5, the block_table read loop).
+ *   orc_kv_write_fp8, orc_attention_kv
+ *                  -- the same write and read with an FP8 cache: each stored
+ *                     element is an FP8 E4M3 code of the value divided by a
+ *                     per-tensor scale, read back as code value times scale
+ *                     ("How vLLM Works Internally: A Deep Dive", "FP8 KV
+ *                     Cache"; "Inside vLLM...", Part 5: the write call takes
+ *                     kv_cache_dtype, k_scale and v_scale).
  *
  * Cache layout (an interface fact, not part of the method; the pages leave the
  * layout open): K pool [num_blocks][num_kv_heads][block_size][head_dim],
@@ -55,6 +62,7 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_FP8 2  /* cache elements: FP8 E4M3 codes, one scale per pool */
 
 /* ------------------------------------------------------------------------ */
 /* prepare                                                                   */
@@ -188,6 +196,132 @@ int orc_kv_write(const void* key, const void* value, int64_t key_row_stride,
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 cache                                                                 */
+/* ------------------------------------------------------------------------ */
+
+static double orc_load(const void* base, int64_t idx, int32_t dtype);
+
+/*
+ * FP8 E4M3 in the OCP 8-bit floating point format (the "fn" variant: no
+ * infinities).  Bit 7 is the sign, bits 6..3 the exponent field E (bias 7),
+ * bits 2..0 the mantissa M.  E = 1..15 encodes (1 + M/8) * 2^(E-7), except
+ * E = 15 with M = 7, which is NaN; E = 0 encodes the subnormal (M/8) * 2^-6.
+ * The largest finite magnitude is 1.75 * 2^8 = 448.  The pages name the FP8
+ * cache but not the format; E4M3 with a per-tensor scale is the plainest
+ * reading of an "fp8" cache dtype that comes with k_scale and v_scale.
+ */
+double orc_fp8_decode(uint8_t code) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  return (code & 0x80) ? -mag : mag;
+}
+
+/*
+ * The E4M3 code of x: the nearest representable value, ties to the even
+ * mantissa; finite magnitudes at or above 448 saturate to +-448 (there is no
+ * infinity to round to); NaN gives the NaN code with x's sign.
+ */
+uint8_t orc_fp8_encode(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return sign | 0x7F;
+  const double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a == 0.0) return sign;
+  /* spacing of representable values around a: 2^(k-3) in the binade
+   * [2^k, 2^(k+1)) for k >= -6, and 2^-9 below 2^-6 (the subnormals) */
+  int k;
+  frexp(a, &k);
+  k -= 1;
+  const double q = (k < -6) ? ldexp(1.0, -9) : ldexp(1.0, k - 3);
+  const double v = rint(a / q) * q; /* a / q is exact; rint rounds half to even */
+  if (v == 0.0) return sign;
+  if (v < ldexp(1.0, -6)) return sign | (uint8_t)(v / ldexp(1.0, -9));
+  int e;
+  frexp(v, &e);
+  e -= 1; /* v in [2^e, 2^(e+1)) */
+  const int m = (int)(v / ldexp(1.0, e - 3)) - 8;
+  return sign | (uint8_t)(((e + 7) << 3) | m);
+}
+
+/* Byte of (block, head, token, dim) in an FP8 K pool: token-major like the
+ * 16-bit pools, [num_blocks][num_kv_heads][block_size][head_dim]. */
+static int64_t orc_k8_byte(int64_t block, int32_t head, int32_t tok, int32_t dim,
+                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim) {
+  return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;
+}
+
+/* Byte of (block, head, token, dim) in an FP8 V pool (block_size 16, head_dim
+ * a multiple of 64).  Each (block, head) run of head_dim * 16 bytes is laid
+ * out as [dim / 64][token / 4][dim % 16][(dim / 16) % 4][token % 4]: sixteen
+ * consecutive bytes hold four tokens of four dims 16 apart.  An interface
+ * fact of the library's pools (the pages leave the layout open). */
+static int64_t orc_v8_byte(int64_t block, int32_t head, int32_t tok, int32_t dim,
+                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim) {
+  const int64_t run = (block * num_kv_heads + head) * (int64_t)head_dim * block_size;
+  const int32_t within =
+      ((((dim / 64) * 4 + tok / 4) * 16 + dim % 16) * 4 + (dim / 16) % 4) * 4 + tok % 4;
+  return run + within;
+}
+
+/*
+ * The FP8 form of orc_kv_write: for every token i with slot s >= 0 and every
+ * kv head h and dim c, the K pool byte of (s / bs, h, s % bs, c) becomes
+ * orc_fp8_encode(k / k_scale) with k = key[i][h][c] and the division done in
+ * binary32, and the V pool byte likewise with v_scale.  key/value hold
+ * elem_bytes = 2 (bf16) or 4 (fp32) elements.  block_size must be 16 and
+ * head_dim a multiple of 64; k_scale and v_scale positive and finite.
+ * Rejects slots outside the pool and duplicate slots.
+ */
+int orc_kv_write_fp8(const void* key, const void* value, int64_t key_row_stride,
+                     int64_t value_row_stride, uint8_t* key_cache, uint8_t* value_cache,
+                     int64_t num_blocks, const int64_t* slot_mapping, int32_t num_tokens,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t elem_bytes, float k_scale, float v_scale) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 64 != 0 ||
+      block_size != 16 || (elem_bytes != 2 && elem_bytes != 4) || !(k_scale > 0.0f) ||
+      !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
+    return ORC_ERR_ARG;
+  if (num_tokens == 0) return ORC_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return ORC_ERR_ARG;
+  const int64_t pool_slots = num_blocks * block_size;
+  int64_t* seen = (int64_t*)malloc(sizeof(int64_t) * (size_t)num_tokens);
+  if (!seen) return ORC_ERR_NOMEM;
+  int32_t n_seen = 0;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t s = slot_mapping[i];
+    if (s < 0) continue;
+    if (s >= pool_slots) { free(seen); return ORC_ERR_RANGE; }
+    seen[n_seen++] = s;
+  }
+  qsort(seen, (size_t)n_seen, sizeof(int64_t), cmp_i64);
+  for (int32_t k = 1; k < n_seen; ++k)
+    if (seen[k] == seen[k - 1]) { free(seen); return ORC_ERR_DUP; }
+  free(seen);
+
+  const int32_t dtype = (elem_bytes == 2) ? ORC_BF16 : ORC_F32;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t s = slot_mapping[i];
+    if (s < 0) continue;
+    const int64_t block = s / block_size;
+    const int32_t off = (int32_t)(s % block_size);
+    for (int32_t h = 0; h < num_kv_heads; ++h) {
+      for (int32_t c = 0; c < head_dim; ++c) {
+        const int64_t src_k = (int64_t)i * key_row_stride + (int64_t)h * head_dim + c;
+        const int64_t src_v = (int64_t)i * value_row_stride + (int64_t)h * head_dim + c;
+        const float kq = (float)orc_load(key, src_k, dtype) / k_scale;
+        const float vq = (float)orc_load(value, src_v, dtype) / v_scale;
+        key_cache[orc_k8_byte(block, h, off, c, num_kv_heads, block_size, head_dim)] =
+            orc_fp8_encode(kq);
+        value_cache[orc_v8_byte(block, h, off, c, num_kv_heads, block_size, head_dim)] =
+            orc_fp8_encode(vq);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* attention                                                                 */
 /* ------------------------------------------------------------------------ */
 
@@ -242,16 +376,26 @@ static int cmp_sel(const void* a, const void* b) {
  * selected row, ORC_ERR_RANGE when a needed table column or block id is out of
  * range.  num_threads <= 0 uses the OpenMP default.
  */
-int orc_attention(const void* q, int64_t q_row_stride, const void* key_cache,
-                  const void* value_cache, int32_t dtype, const int32_t* qsl,
-                  const int32_t* seq_lens, const int32_t* block_table, int64_t bt_stride,
-                  int32_t bt_cols, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
-                  int32_t head_dim, int32_t block_size, int64_t num_blocks, double scale,
-                  const int32_t* rows, int32_t num_rows, double* out, int32_t num_threads) {
+/*
+ * orc_attention_kv is orc_attention with the cache dtype given apart from the
+ * query dtype: kv_dtype = ORC_FP8 reads every K element as
+ * orc_fp8_decode(byte) * k_scale (V likewise with v_scale) from the FP8 pool
+ * layouts above; any other kv_dtype must equal dtype and ignores the scales.
+ * The widening is exact in fp64, so the attention arithmetic is unchanged.
+ */
+int orc_attention_kv(const void* q, int64_t q_row_stride, const void* key_cache,
+                     const void* value_cache, int32_t dtype, int32_t kv_dtype, double k_scale,
+                     double v_scale, const int32_t* qsl, const int32_t* seq_lens,
+                     const int32_t* block_table, int64_t bt_stride, int32_t bt_cols,
+                     int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int64_t num_blocks, double scale,
+                     const int32_t* rows, int32_t num_rows, double* out, int32_t num_threads) {
   if (!q || !key_cache || !value_cache || !qsl || !seq_lens || !block_table || !out ||
       num_reqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_rows < 0 || num_q_heads % num_kv_heads != 0 ||
-      (dtype != ORC_F32 && dtype != ORC_BF16))
+      (dtype != ORC_F32 && dtype != ORC_BF16) ||
+      (kv_dtype != dtype && kv_dtype != ORC_FP8) ||
+      (kv_dtype == ORC_FP8 && (block_size != 16 || head_dim % 64 != 0)))
     return ORC_ERR_ARG;
   const int32_t total_rows = qsl[num_reqs];
   if (!rows && num_rows != total_rows) return ORC_ERR_ARG;
@@ -353,10 +497,21 @@ int orc_attention(const void* q, int64_t q_row_stride, const void* key_cache,
         const int64_t phys = block_table[(int64_t)r * bt_stride + j / block_size];
         const int32_t off = j % block_size;
         for (int32_t c = 0; c < head_dim; ++c) {
-          Kr[(int64_t)j * head_dim + c] = orc_load(
-              key_cache, orc_k_elem(phys, g, off, c, num_kv_heads, block_size, head_dim), dtype);
-          Vr[(int64_t)j * head_dim + c] = orc_load(
-              value_cache, orc_v_elem(phys, g, off, c, num_kv_heads, block_size, head_dim), dtype);
+          if (kv_dtype == ORC_FP8) {
+            Kr[(int64_t)j * head_dim + c] =
+                orc_fp8_decode(((const uint8_t*)key_cache)[orc_k8_byte(
+                    phys, g, off, c, num_kv_heads, block_size, head_dim)]) * k_scale;
+            Vr[(int64_t)j * head_dim + c] =
+                orc_fp8_decode(((const uint8_t*)value_cache)[orc_v8_byte(
+                    phys, g, off, c, num_kv_heads, block_size, head_dim)]) * v_scale;
+          } else {
+            Kr[(int64_t)j * head_dim + c] = orc_load(
+                key_cache, orc_k_elem(phys, g, off, c, num_kv_heads, block_size, head_dim),
+                dtype);
+            Vr[(int64_t)j * head_dim + c] = orc_load(
+                value_cache, orc_v_elem(phys, g, off, c, num_kv_heads, block_size, head_dim),
+                dtype);
+          }
         }
       }
       for (int32_t k = item.first; k < item.first + item.count; ++k) {
@@ -391,6 +546,18 @@ int orc_attention(const void* q, int64_t q_row_stride, const void* key_cache,
   free(items);
   free(sel);
   return status;
+}
+
+int orc_attention(const void* q, int64_t q_row_stride, const void* key_cache,
+                  const void* value_cache, int32_t dtype, const int32_t* qsl,
+                  const int32_t* seq_lens, const int32_t* block_table, int64_t bt_stride,
+                  int32_t bt_cols, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int64_t num_blocks, double scale,
+                  const int32_t* rows, int32_t num_rows, double* out, int32_t num_threads) {
+  return orc_attention_kv(q, q_row_stride, key_cache, value_cache, dtype, dtype, 1.0, 1.0, qsl,
+                          seq_lens, block_table, bt_stride, bt_cols, num_reqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, scale, rows, num_rows,
+                          out, num_threads);
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */

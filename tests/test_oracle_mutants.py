@@ -35,14 +35,24 @@ MUTANTS = {
                               "for (int32_t h = g; h < num_q_heads; h += num_kv_heads) {"),
     "value layout transposed": ("return ((block * num_kv_heads + head) * (int64_t)head_dim + dim) * block_size + tok;",
                                 "return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;"),
-    "gather offset uses block index": ("const int32_t off = j % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          Kr",
-                                       "const int32_t off = (j / block_size) % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          Kr"),
+    "gather offset uses block index": ("const int32_t off = j % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          if (kv_dtype",
+                                       "const int32_t off = (j / block_size) % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          if (kv_dtype"),
     "kv write uses key layout for values": (
         "const int64_t dv = orc_v_elem(block, h, off, c, num_kv_heads, block_size, head_dim);",
         "const int64_t dv = orc_k_elem(block, h, off, c, num_kv_heads, block_size, head_dim);"),
     "bf16 widening wrong half": ("uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;",
                                  "uint32_t bits = (uint32_t)((const uint16_t*)base)[idx];"),
     "normaliser dropped": ("const double wj = s[j] / denom;", "const double wj = s[j];"),
+    "fp8 exponent bias off by one": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "fp8 subnormals scaled as normals": ("ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    "fp8 rounds half away from zero": ("const double v = rint(a / q) * q;",
+                                       "const double v = floor(a / q + 0.5) * q;"),
+    "fp8 no saturation": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 448.0) return sign | 0x7F;"),
+    "fp8 write multiplies by the scale": ("(float)orc_load(key, src_k, dtype) / k_scale;",
+                                          "(float)orc_load(key, src_k, dtype) * k_scale;"),
+    "fp8 read ignores the value scale": ("phys, g, off, c, num_kv_heads, block_size, head_dim)]) * v_scale;",
+                                         "phys, g, off, c, num_kv_heads, block_size, head_dim)]);"),
+    "fp8 value layout collides": ("* 4 + (dim / 16) % 4) * 4 + tok % 4;", "* 4 + (dim / 32) % 4) * 4 + tok % 4;"),
 }
 
 

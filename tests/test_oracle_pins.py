@@ -452,3 +452,176 @@ def test_prepare_write_attention_chain_equals_unpaged_sdpa():
     out = oracle.attention(paged["q"], kc, vc, prep["query_start_loc"], prep["seq_lens"],
                            paged["bt"], 4, 0.25)
     assert np.max(np.abs(out - sdpa_reference(logical, 0.25))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# FP8 cache ("How vLLM Works Internally: A Deep Dive", "FP8 KV Cache"; the
+# write call's kv_cache_dtype / k_scale / v_scale, "Inside vLLM...", Part 5).
+# The format is OCP FP8 E4M3; torch's float8_e4m3fn is an independent
+# implementation of the same format.
+# ---------------------------------------------------------------------------
+
+def _fp8_table():
+    return np.array([oracle.fp8_decode(c) for c in range(256)])
+
+
+def test_fp8_decode_matches_torch_float8_e4m3fn_for_every_code():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = _fp8_table()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_format_landmarks():
+    # largest finite 448 = 1.75 * 2^8, one = bias 7, smallest subnormal 2^-9,
+    # no infinities: the all-ones codes are the only NaNs
+    assert oracle.fp8_decode(0x7E) == 448.0 and oracle.fp8_decode(0xFE) == -448.0
+    assert oracle.fp8_decode(0x38) == 1.0
+    assert oracle.fp8_decode(0x01) == 2.0 ** -9 and oracle.fp8_decode(0x08) == 2.0 ** -6
+    assert [c for c in range(256) if math.isnan(oracle.fp8_decode(c))] == [0x7F, 0xFF]
+
+
+def test_fp8_encode_round_trips_every_code():
+    for c in range(256):
+        v = oracle.fp8_decode(c)
+        if not math.isnan(v):
+            assert oracle.fp8_encode(v) == c, hex(c)
+
+
+def test_fp8_encode_is_nearest_with_ties_to_even():
+    table = _fp8_table()
+    finite = [c for c in range(256) if not math.isnan(table[c])]
+    vals = np.array([table[c] for c in finite])
+    rng = np.random.default_rng(3)
+    # random magnitudes over the whole range, plus every exact midpoint
+    xs = list(rng.standard_normal(4000) * 40) + list(rng.uniform(-2 ** -5, 2 ** -5, 2000))
+    pos = np.unique(np.abs(vals))
+    xs += list((pos[1:] + pos[:-1]) / 2) + list(-(pos[1:] + pos[:-1]) / 2)
+    for x in xs:
+        x32 = float(np.float32(x))
+        c = oracle.fp8_encode(x32)
+        v = oracle.fp8_decode(c)
+        d = np.abs(vals - x32)
+        best = d.min()
+        assert abs(v - x32) == best, (x32, hex(c))
+        ties = [finite[i] for i in np.nonzero(d == best)[0] if (finite[i] & 0x7F) or x32 == 0]
+        if len(ties) > 1 and x32 != 0:
+            assert c & 1 == 0, (x32, hex(c))  # ties go to the even mantissa
+
+
+def test_fp8_encode_matches_torch_in_range():
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(20000) * 30, rng.standard_normal(5000) * 1e-2])
+    x = x[np.abs(x) < 440].astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_encode(v) for v in x], np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_fp8_encode_saturates_and_keeps_nan():
+    assert oracle.fp8_encode(449.0) == 0x7E and oracle.fp8_encode(1e30) == 0x7E
+    assert oracle.fp8_encode(-float("inf")) == 0xFE
+    assert oracle.fp8_encode(float("nan")) & 0x7F == 0x7F
+    assert oracle.fp8_encode(-0.0) == 0x80 and oracle.fp8_encode(2.0 ** -11) == 0x00
+
+
+def _fp8_case(seed, T=6, H=2, d=128, nb=5):
+    g = torch.Generator().manual_seed(seed)
+    key = torch.randn(T, H, d, generator=g).to(torch.bfloat16)
+    value = torch.randn(T, H, d, generator=g).to(torch.bfloat16)
+    slots = np.array([3, 17, -1, 40, 79, 64], np.int64)[:T]
+    return key, value, slots, nb
+
+
+def test_fp8_kv_write_touches_only_written_slots():
+    key, value, slots, nb = _fp8_case(1)
+    kc = np.full((nb, 2, 16, 128), 0x55, np.uint8)
+    vc = np.full((nb, 2, 128 * 16), 0x55, np.uint8)
+    oracle.kv_write_fp8(key, value, kc, vc, slots, 16, 0.75, 1.5)
+    n_written = int((slots >= 0).sum()) * 2 * 128
+    for pool in (kc, vc):
+        changed = int((pool != 0x55).sum())
+        assert n_written - 64 <= changed <= n_written  # a code may equal the filler
+    # blocks no slot names are untouched
+    hit = {int(s) // 16 for s in slots if s >= 0}
+    for blk in range(nb):
+        if blk not in hit:
+            assert (kc[blk] == 0x55).all() and (vc[blk] == 0x55).all()
+
+
+def test_fp8_value_row_reads_back_dequantized():
+    """A one-key context returns its V row exactly: each element is
+    fp8_decode(fp8_encode(v / v_scale)) * v_scale, the division in binary32."""
+    key, value, _, _ = _fp8_case(6)
+    ks, vs = 0.75, 1.5
+    for i in range(key.shape[0]):
+        kc1 = np.zeros((1, 2, 16, 128), np.uint8)
+        vc1 = np.zeros((1, 2, 128 * 16), np.uint8)
+        oracle.kv_write_fp8(key[i:i + 1], value[i:i + 1], kc1, vc1, [0], 16, ks, vs)
+        q = torch.randn(1, 2, 128).to(torch.bfloat16)
+        out = oracle.attention(q, kc1, vc1, [0, 1], [1], [[0]], 16, 1.0, kv_scales=(ks, vs))
+        for h in range(2):
+            v_exp = [oracle.fp8_decode(oracle.fp8_encode(np.float32(x) / np.float32(vs))) * vs
+                     for x in value[i, h].float().numpy()]
+            assert np.array_equal(out[0, h], np.array(v_exp))
+
+
+def test_fp8_attention_equals_16bit_attention_on_dequantized_pools():
+    """Attention over an FP8 pool equals attention over a bf16 pool holding
+    code x scale for every element (exact in bf16 for power-of-two scales)."""
+    rng = np.random.default_rng(8)
+    nst, nct = [1, 5, 1, 20], [40, 3, 70, 0]
+    R, H, Hq, d, bs = 4, 2, 8, 128, 16
+    seq = [a + b for a, b in zip(nst, nct)]
+    need = [-(-L // bs) for L in seq]
+    nb = sum(need) + 3
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((R, max(need)), -1, np.int32)
+    cur = 0
+    for r in range(R):
+        bt[r, :need[r]] = perm[cur:cur + need[r]]
+        cur += need[r]
+    g = torch.Generator().manual_seed(9)
+    T = sum(nst)
+    all_k = torch.randn(nb * bs, H, d, generator=g).to(torch.bfloat16)
+    all_v = torch.randn(nb * bs, H, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(T, Hq, d, generator=g).to(torch.bfloat16)
+    ks, vs = 0.25, 2.0
+    kc8 = np.zeros((nb, H, bs, d), np.uint8)
+    vc8 = np.zeros((nb, H, d * bs), np.uint8)
+    slots = np.arange(nb * bs, dtype=np.int64)
+    oracle.kv_write_fp8(all_k, all_v, kc8, vc8, slots, bs, ks, vs)
+    deq = np.vectorize(lambda x, s: oracle.fp8_decode(oracle.fp8_encode(np.float32(x) / np.float32(s))) * s)
+    kd = torch.from_numpy(deq(all_k.float().numpy(), ks).astype(np.float32)).to(torch.bfloat16)
+    vd = torch.from_numpy(deq(all_v.float().numpy(), vs).astype(np.float32)).to(torch.bfloat16)
+    kc16 = torch.zeros(nb, H, bs, d, dtype=torch.bfloat16)
+    vc16 = torch.zeros(nb, H, d, bs, dtype=torch.bfloat16)
+    oracle.kv_write(kd, vd, kc16, vc16, slots, bs)
+    qsl = np.concatenate([[0], np.cumsum(nst)]).astype(np.int32)
+    ref = oracle.attention(q, kc16, vc16, qsl, seq, bt, bs, 1 / math.sqrt(d))
+    got = oracle.attention(q, kc8, vc8, qsl, seq, bt, bs, 1 / math.sqrt(d), kv_scales=(ks, vs))
+    assert np.array_equal(got, ref)
+
+
+def test_fp8_value_layout_fills_every_byte_of_a_run():
+    """Writing all 16 tokens of a block touches every byte of its V run once."""
+    g = torch.Generator().manual_seed(2)
+    key = torch.randn(16, 1, 128, generator=g).to(torch.bfloat16) + 3.0  # no zero codes
+    value = torch.randn(16, 1, 128, generator=g).to(torch.bfloat16) + 3.0
+    kc = np.zeros((1, 1, 16, 128), np.uint8)
+    vc = np.zeros((1, 1, 128 * 16), np.uint8)
+    oracle.kv_write_fp8(key, value, kc, vc, np.arange(16), 16, 1.0, 1.0)
+    assert (vc != 0).all() and (kc != 0).all()
+
+
+def test_fp8_write_rejects_bad_arguments():
+    key, value, slots, nb = _fp8_case(5)
+    kc = np.zeros((nb, 2, 16, 128), np.uint8)
+    vc = np.zeros((nb, 2, 128 * 16), np.uint8)
+    for ks in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(oracle.OracleError):
+            oracle.kv_write_fp8(key, value, kc, vc, slots, 16, ks, 1.0)
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_write_fp8(key, value, kc, vc, np.array([3, 3, -1, 4, 5, 6]), 16, 1.0, 1.0)
