@@ -9,6 +9,8 @@
  *                              per-request token counts and block tables;
  *   pkv_kv_cache_write         each new token's K and V rows into the block
  *                              pool at its slot;
+ *   pkv_kv_cache_write_fp8     the same into an FP8 E4M3 pool with a scale
+ *                              per pool;
  *   pkv_paged_attention_varlen causal attention of every query row of the
  *                              step (prefill chunks and single-token decodes
  *                              alike, in one launch) over its request's
@@ -147,6 +149,51 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, int64_t key_ro
                               int64_t num_blocks, const int64_t* slot_mapping,
                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_kv_cache_write_fp8 -- pkv_kv_cache_write into an FP8 cache.
+ *
+ * Follows "Inside vLLM: Following One Request from the API to GPU
+ * Execution", Part 5 (the write call takes kv_cache_dtype, k_scale and
+ * v_scale next to the pools) and "How vLLM Works Internally: A Deep Dive",
+ * "FP8 KV Cache" (the cache is stored in FP8 instead of 16-bit floats).
+ * Reading of the pages: the FP8 format is OCP E4M3 (no infinities, largest
+ * finite 448) and each pool has one scale.  For every i with
+ * s = slot_mapping[i] in [0, num_blocks * 16), every kv head h and dim c:
+ *   K byte (s / 16, h, s % 16, c) = e4m3(key[i][h][c] / *k_scale)
+ *   V byte (s / 16, h, s % 16, c) = e4m3(value[i][h][c] / *v_scale)
+ * where the division is binary32 and e4m3() rounds to the nearest code, ties
+ * to even, saturating finite magnitudes beyond 448 (NaN stays NaN).  A code
+ * reads back as its E4M3 value times the scale.
+ *
+ * FP8 pool layouts (bytes; block_size 16, head_dim a multiple of 64):
+ *   K pool: [num_blocks][num_kv_heads][16][head_dim]            (token-major)
+ *   V pool: [num_blocks][num_kv_heads][head_dim * 16], each (block, head) run
+ *           ordered [dim / 64][token / 4][dim % 16][(dim / 16) % 4][token % 4],
+ *           so 16 consecutive bytes hold 4 tokens of 4 dims 16 apart -- one
+ *           16-byte load of the attention kernels.
+ *
+ * Arguments (device pointers unless stated):
+ *   key, value      [num_tokens][num_kv_heads][head_dim] of `dtype` (PKV_BF16 or
+ *                   PKV_F32); row i starts at element i * key_row_stride
+ *                   (value_row_stride); heads and dims contiguous in a row
+ *   key_cache, value_cache  the FP8 pools above, 16-byte aligned
+ *   num_blocks      host, blocks in each pool
+ *   slot_mapping    int64 [num_tokens]; < 0 (padding) or past the pool: skipped
+ *   num_tokens, num_kv_heads, head_dim, block_size   host
+ *   k_scale, v_scale  float32 scalars, positive and finite (preconditions)
+ * Preconditions: slots unique within a call.
+ * Errors: PKV_ERR_INVALID_ARG (null pointers with num_tokens > 0, sizes < 1,
+ * row strides < num_kv_heads * head_dim, misaligned pointers);
+ * PKV_ERR_UNSUPPORTED (block_size != 16, head_dim not a multiple of 64 or
+ * > 256); PKV_ERR_LAUNCH.
+ */
+pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, int64_t key_row_stride,
+                                  int64_t value_row_stride, void* key_cache, void* value_cache,
+                                  int64_t num_blocks, const int64_t* slot_mapping,
+                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, pkv_dtype dtype, const float* k_scale,
+                                  const float* v_scale, void* stream);
 
 /*
  * pkv_paged_attention_workspace_bytes -- device workspace that

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 EXPORTS = ("pkv_status_string", "pkv_prepare_inputs", "pkv_kv_cache_write",
-           "pkv_paged_attention_workspace_bytes", "pkv_paged_attention_varlen")
+           "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
+           "pkv_paged_attention_varlen")
 
 
 class PkvError(RuntimeError):
@@ -47,6 +48,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_kv_cache_write.argtypes = [P, P, i64, i64, P, P, i64, P, i32, i32, i32, i32,
                                        ctypes.c_int, P]
     lib.pkv_kv_cache_write.restype = ctypes.c_int
+    lib.pkv_kv_cache_write_fp8.argtypes = [P, P, i64, i64, P, P, i64, P, i32, i32, i32, i32,
+                                           ctypes.c_int, P, P, P]
+    lib.pkv_kv_cache_write_fp8.restype = ctypes.c_int
     lib.pkv_paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                                         ctypes.c_int]
     lib.pkv_paged_attention_workspace_bytes.restype = sz
@@ -133,6 +137,25 @@ def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
         key_cache.shape[0], _dev(slot_mapping, torch.int64, "slot_mapping"), T, H, d,
         int(block_size), _dtype_code(key.dtype), _stream(key.device))
     _check(st, "pkv_kv_cache_write")
+
+
+def kv_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                       k_scale: torch.Tensor, v_scale: torch.Tensor, *, block_size: int) -> None:
+    """pkv_kv_cache_write_fp8.  key/value: [T, Hkv, d] (bf16 or fp32) with
+    contiguous rows; pools are uint8 tensors in the FP8 layouts (K [nb, Hkv,
+    16, d], V [nb, Hkv, d * 16]); scales are one-element float32 device tensors."""
+    T, H, d = key.shape
+    for t in (key, value):
+        assert t.stride(2) == 1 and t.stride(1) == d, "heads and dims must be contiguous"
+    assert key_cache.is_contiguous() and value_cache.is_contiguous()
+    st = load().pkv_kv_cache_write_fp8(
+        _dev(key, name="key"), _dev(value, name="value"), key.stride(0), value.stride(0),
+        _dev(key_cache, torch.uint8, "key_cache"), _dev(value_cache, torch.uint8, "value_cache"),
+        key_cache.shape[0], _dev(slot_mapping, torch.int64, "slot_mapping"), T, H, d,
+        int(block_size), _dtype_code(key.dtype), _dev(k_scale, torch.float32, "k_scale"),
+        _dev(v_scale, torch.float32, "v_scale"), _stream(key.device))
+    _check(st, "pkv_kv_cache_write_fp8")
 
 
 def attention_workspace_bytes(num_reqs: int, num_tokens: int, num_q_heads: int,

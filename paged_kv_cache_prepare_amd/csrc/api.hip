@@ -74,6 +74,36 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, int64_t key_ro
                                             static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, int64_t key_row_stride,
+                                  int64_t value_row_stride, void* key_cache, void* value_cache,
+                                  int64_t num_blocks, const int64_t* slot_mapping,
+                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, pkv_dtype dtype, const float* k_scale,
+                                  const float* v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (block_size != pkv::kBlock || head_dim % 64 != 0 || head_dim > 256)
+    return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  const int32_t esz = dtype == PKV_BF16 ? 2 : 4;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping || !k_scale || !v_scale)
+    return PKV_ERR_INVALID_ARG;
+  if (key_row_stride < row || value_row_stride < row) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(key_cache) || !aligned16(value_cache) ||
+      (reinterpret_cast<uintptr_t>(key) & (esz - 1)) != 0 ||
+      (reinterpret_cast<uintptr_t>(value) & (esz - 1)) != 0 ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3) != 0 ||
+      (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_kv_write_fp8(key, value, key_row_stride, value_row_stride,
+                                                key_cache, value_cache, num_blocks, slot_mapping,
+                                                num_tokens, num_kv_heads, head_dim, esz, k_scale,
+                                                v_scale, static_cast<hipStream_t>(stream)));
+}
+
 size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_query_len,

@@ -112,7 +112,158 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
   }
 }
 
+// FP8 E4M3 cache ("How vLLM Works Internally: A Deep Dive", "FP8 KV Cache";
+// the write call's kv_cache_dtype, k_scale and v_scale): each element is
+// stored as the E4M3 code of value / scale (binary32 division, nearest with
+// ties to even; finite magnitudes beyond 448 saturate).
+//  * K pool: [block][head][offset][dim] bytes, one 16-byte store per 16 dims.
+//  * V pool: each (block, head) run of head_dim * 16 bytes is
+//    [dim / 64][offset / 4][dim % 16][(dim / 16) % 4][offset % 4]: 16
+//    consecutive bytes are 4 tokens of 4 dims 16 apart, the unit the
+//    attention kernels load.  The tile's codes are staged in LDS; a 16-byte
+//    unit is stored whole when its 4 tokens are this tile's consecutive
+//    slots of one block (a prompt chunk), byte by byte otherwise.
+__device__ inline float fp8_prescale(float x, float scale) {
+  const float q = x / scale;
+  return (q != q) ? q : fminf(fmaxf(q, -448.f), 448.f);  // NaN stays NaN
+}
+
+// E4M3 codes of four values, element 0 in the low byte.
+__device__ inline unsigned fp8x4(float a, float b, float c, float d) {
+  unsigned w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+template <int E>  // element bytes of key/value: 2 (bf16) or 4 (fp32)
+__device__ inline float load_elem(const char* p) {
+  if (E == 2) {
+    const unsigned bits = (unsigned)*reinterpret_cast<const uint16_t*>(p) << 16;
+    return __builtin_bit_cast(float, bits);
+  }
+  return *reinterpret_cast<const float*>(p);
+}
+
+constexpr int kMaxDim8 = 256;
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, int64_t key_stride,
+    int64_t value_stride, uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
+    int64_t num_blocks, const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
+    int32_t num_kv_heads, int32_t head_dim, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
+  __shared__ uint8_t s_v[kTileTokens][kMaxDim8];
+  __shared__ int64_t s_slot[kTileTokens];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTileTokens;
+  const int h = blockIdx.y;
+  const int64_t pool_slots = num_blocks * kTileTokens;
+  const float ks = *k_scale, vs = *v_scale;
+  const int64_t run = (int64_t)head_dim * kTileTokens;  // bytes of one (block, head) run
+
+  if (tid < kTileTokens) {
+    int64_t s = -1;
+    if (t0 + tid < num_tokens) {
+      s = slot_mapping[t0 + tid];
+      if (s >= pool_slots) s = -1;
+    }
+    s_slot[tid] = s < 0 ? -1 : s;
+  }
+  __syncthreads();
+
+  // K rows (and the V codes into LDS): one task = 16 dims of one token
+  const int chunks = head_dim / 16;
+  for (int w = tid; w < kTileTokens * chunks; w += kThreads) {
+    const int tk = w / chunks;
+    const int c = w - tk * chunks;
+    const int64_t s = s_slot[tk];
+    if (s < 0) continue;
+    const int64_t row = t0 + tk;
+    const char* kp = key + (row * key_stride + (int64_t)h * head_dim + 16 * c) * E;
+    const char* vp = value + (row * value_stride + (int64_t)h * head_dim + 16 * c) * E;
+    unsigned kw[4], vw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float k4[4], v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        k4[j] = fp8_prescale(load_elem<E>(kp + (4 * i + j) * E), ks);
+        v4[j] = fp8_prescale(load_elem<E>(vp + (4 * i + j) * E), vs);
+      }
+      kw[i] = fp8x4(k4[0], k4[1], k4[2], k4[3]);
+      vw[i] = fp8x4(v4[0], v4[1], v4[2], v4[3]);
+    }
+    const int64_t blk = s / kTileTokens;
+    const int64_t off = s - blk * kTileTokens;
+    *reinterpret_cast<u32x4*>(key_cache + (blk * num_kv_heads + h) * run + off * head_dim +
+                              16 * c) = u32x4{kw[0], kw[1], kw[2], kw[3]};
+    *reinterpret_cast<u32x4*>(&s_v[tk][16 * c]) = u32x4{vw[0], vw[1], vw[2], vw[3]};
+  }
+  __syncthreads();
+
+  // V: one task = one 16-byte unit (4 tokens of the tile x 4 dims 16 apart)
+  const int quads = head_dim / 64;
+  for (int w = tid; w < 4 * quads * 16; w += kThreads) {
+    const int n = w & 15;
+    const int dq = (w >> 4) % quads;
+    const int tg = w / (16 * quads);  // tokens 4tg..4tg+3 of the tile
+    const int tk0 = 4 * tg;
+    const int64_t s0 = s_slot[tk0];
+    uint8_t b[16];  // b[4 dt + tt] = token tk0 + tt, dim 64 dq + 16 dt + n
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) b[4 * dt + tt] = s_v[tk0 + tt][64 * dq + 16 * dt + n];
+    bool whole = s0 >= 0 && (s0 & 3) == 0;
+#pragma unroll
+    for (int tt = 1; tt < 4; ++tt) whole = whole && s_slot[tk0 + tt] == s0 + tt;
+    if (whole) {
+      const int64_t blk = s0 / kTileTokens;
+      const int g = (int)(s0 - blk * kTileTokens) / 4;
+      u32x4 v;
+      __builtin_memcpy(&v, b, 16);
+      *reinterpret_cast<u32x4*>(value_cache + (blk * num_kv_heads + h) * run +
+                                (((int64_t)dq * 4 + g) * 16 + n) * 16) = v;
+      continue;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int64_t s = s_slot[tk0 + tt];
+      if (s < 0) continue;
+      const int64_t blk = s / kTileTokens;
+      const int off = (int)(s - blk * kTileTokens);
+      uint8_t* unit = value_cache + (blk * num_kv_heads + h) * run +
+                      (((int64_t)dq * 4 + off / 4) * 16 + n) * 16 + off % 4;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) unit[4 * dt] = b[4 * dt + tt];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_write_fp8(const void* key, const void* value, int64_t key_stride,
+                               int64_t value_stride, void* key_cache, void* value_cache,
+                               int64_t num_blocks, const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t elem_bytes, const float* k_scale, const float* v_scale,
+                               hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  dim3 grid((num_tokens + kTileTokens - 1) / kTileTokens, num_kv_heads);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<2>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const char*>(key), static_cast<const char*>(value),
+                       key_stride, value_stride, static_cast<uint8_t*>(key_cache),
+                       static_cast<uint8_t*>(value_cache), num_blocks, slot_mapping, num_tokens,
+                       num_kv_heads, head_dim, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(kv_write_fp8_kernel<4>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const char*>(key), static_cast<const char*>(value),
+                       key_stride, value_stride, static_cast<uint8_t*>(key_cache),
+                       static_cast<uint8_t*>(value_cache), num_blocks, slot_mapping, num_tokens,
+                       num_kv_heads, head_dim, k_scale, v_scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_write(const void* key, const void* value, int64_t key_stride,
                            int64_t value_stride, void* key_cache, void* value_cache,

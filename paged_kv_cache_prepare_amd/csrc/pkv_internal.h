@@ -46,6 +46,13 @@ hipError_t launch_kv_write(const void* key, const void* value, int64_t key_strid
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t elem_bytes, hipStream_t stream);
 
+hipError_t launch_kv_write_fp8(const void* key, const void* value, int64_t key_stride,
+                               int64_t value_stride, void* key_cache, void* value_cache,
+                               int64_t num_blocks, const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t elem_bytes, const float* k_scale, const float* v_scale,
+                               hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   int64_t q_stride;

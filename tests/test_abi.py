@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "pkv.h")
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\S.*?\b(pkv_[a-z_]+)\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(pkv_[a-z0-9_]+)\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")

@@ -194,3 +194,69 @@ def test_kv_write_configs(idx):
     oracle.kv_write(wl.key.cpu(), wl.value.cpu(), okc, ovc, ref["slot_mapping"], wl.block_size)
     assert torch.equal(bits_view(kc.cpu()), bits_view(okc)), "K pool"
     assert torch.equal(bits_view(vc.cpu()), bits_view(ovc)), "V pool"
+
+
+# ---------------------------------------------------------------------------
+# FP8 cache write: E4M3 codes of value / scale must match the oracle byte
+# for byte (the quantised code is an integer decision taken in binary32 on
+# both sides).
+# ---------------------------------------------------------------------------
+
+def _fp8_scales(dev, ks, vs):
+    return (torch.tensor([ks], dtype=torch.float32, device=dev),
+            torch.tensor([vs], dtype=torch.float32, device=dev))
+
+
+def test_kv_write_fp8_rounding_matches_oracle():
+    """Every E4M3 value, every midpoint between neighbours (ties), values just
+    off the midpoints, subnormals, saturation and zeros, through the kernel's
+    conversion with scale 1, against the oracle's encoder."""
+    table = np.array([oracle.fp8_decode(c) for c in range(256)])
+    pos = np.unique(np.abs(table[~np.isnan(table)]))
+    mids = (pos[1:] + pos[:-1]) / 2
+    vals = np.concatenate([pos, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9)),
+                           [447.9, 448.0, 460.0, 464.0, 470.0, 1e6, 2.0 ** -10, 2.0 ** -11, 0.0]])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    d = 128
+    T = -(-len(vals) // d)
+    flat = np.zeros(T * d, np.float32)
+    flat[:len(vals)] = vals
+    key = torch.from_numpy(flat.reshape(T, 1, d))
+    val = key.clone()
+    dev = device()
+    nb = -(-T // 16)
+    kc = torch.zeros(nb, 1, 16, d, dtype=torch.uint8, device=dev)
+    vc = torch.zeros(nb, 1, d * 16, dtype=torch.uint8, device=dev)
+    ks, vs = _fp8_scales(dev, 1.0, 1.0)
+    pkv.kv_cache_write_fp8(key.to(dev), val.to(dev), kc, vc, torch.arange(T, device=dev), ks, vs,
+                           block_size=16)
+    torch.cuda.synchronize()
+    got = kc.cpu().numpy().reshape(-1)[:len(vals)]
+    want = np.array([oracle.fp8_encode(v) for v in vals], np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert len(bad) == 0, [(float(vals[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("consecutive", [False, True])
+def test_kv_write_fp8_vs_oracle(dtype, d, consecutive):
+    T, H, nb, bs = 77, 3, 40, 16
+    key, val, _, _, slots = _kv_case(T, H, d, bs, nb, dtype, 11 + d, consecutive)
+    key, val = key * 3, val * 0.5
+    g = torch.Generator().manual_seed(d)
+    kc = torch.randint(0, 256, (nb, H, bs, d), generator=g, dtype=torch.uint8)
+    vc = torch.randint(0, 256, (nb, H, d * bs), generator=g, dtype=torch.uint8)
+    okc, ovc = kc.clone(), vc.clone()
+    oslots = slots.copy()
+    oslots[oslots >= nb * bs] = -1
+    oracle.kv_write_fp8(key, val, okc, ovc, oslots, bs, 0.37, 2.5)
+    dev = device()
+    gkc, gvc = kc.to(dev), vc.to(dev)
+    ks, vs = _fp8_scales(dev, 0.37, 2.5)
+    pkv.kv_cache_write_fp8(key.to(dev), val.to(dev), gkc, gvc, torch.from_numpy(slots).to(dev),
+                           ks, vs, block_size=bs)
+    torch.cuda.synchronize()
+    assert torch.equal(gkc.cpu(), okc)
+    assert torch.equal(gvc.cpu(), ovc)
