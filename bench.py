@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "attn tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP8_SCALES = (0.0125, 0.0125)    # k_scale, v_scale of --kv-dtype fp8 (N(0,1) history / scale)
 
 
 def parse():
@@ -50,6 +51,9 @@ def parse():
                    help="context partition size of decode items (0 = library default)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate budget of the CPU oracle baseline")
+    p.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                   help="cache element type: bf16, or FP8 E4M3 codes with per-pool scales "
+                        "(the same history quantised; q and out stay bf16)")
     p.add_argument("--graph", action="store_true",
                    help="also capture the step in a HIP graph and time K replays; value and "
                         "ms_per_step then come from the replays")
@@ -85,8 +89,9 @@ def algorithmic_work(wl):
     nst = wl.num_scheduled_tokens.astype(np.int64)
     seq = nst + wl.num_computed_tokens.astype(np.int64)
     e = 2 if str(wl.dtype).endswith("bfloat16") else 4
+    e_kv = 1 if wl.kv_scales is not None else e  # FP8 pools: one byte per element
     Hq, Hkv, d, bs = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
-    kv_token_bytes = 2 * Hkv * d * e
+    kv_token_bytes = 2 * Hkv * d * e_kv
     # unique context tokens: blocks shared by several requests are read once
     shared = 0
     if wl.notes.get("shared_blocks"):
@@ -113,7 +118,7 @@ def algorithmic_work(wl):
         "bytes_unique": unique_ctx * kv_token_bytes + q_o_bytes + table_bytes,
         "flops_decode": pairs_dec * flops_per_pair,
         "flops_prefill": pairs_pre * flops_per_pair,
-        "write_bytes": 2 * 2 * T * Hkv * d * e,
+        "write_bytes": 2 * T * Hkv * d * (e + e_kv),
     }
 
 
@@ -162,13 +167,16 @@ def cpu_baseline(wl, budget_s):
     t0 = time.perf_counter()
     prep = oracle.prepare(wl.num_scheduled_tokens, wl.num_computed_tokens, wl.block_table,
                           wl.block_size, wl.num_blocks)
-    oracle.kv_write(key, val, kc, vc, prep["slot_mapping"], wl.block_size)
+    if wl.kv_scales is None:
+        oracle.kv_write(key, val, kc, vc, prep["slot_mapping"], wl.block_size)
+    else:
+        oracle.kv_write_fp8(key, val, kc, vc, prep["slot_mapping"], wl.block_size, *wl.kv_scales)
     t_pw = time.perf_counter() - t0
 
     def attn(rows):
         t1 = time.perf_counter()
         oracle.attention(q, kc, vc, prep["query_start_loc"], prep["seq_lens"], wl.block_table,
-                         wl.block_size, wl.scale, rows=rows)
+                         wl.block_size, wl.scale, rows=rows, kv_scales=wl.kv_scales)
         return time.perf_counter() - t1
 
     n = min(T, 2 * threads)
@@ -208,6 +216,11 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = workloads.config(args.workload, device=dev)
+    if args.kv_dtype == "fp8":
+        if wl.dtype != torch.bfloat16:
+            print("an FP8 cache needs bf16 queries (workloads 2-5)", file=sys.stderr)
+            sys.exit(2)
+        wl = workloads.to_fp8(wl, *FP8_SCALES)
     if args.rows != "all":
         group = wl.num_q_heads // wl.num_kv_heads
         short = wl.num_scheduled_tokens * group <= 16
@@ -227,6 +240,10 @@ def main():
             "query_start_loc": torch.empty(R + 1, **i32), "seq_lens": torch.empty(R, **i32),
             "logits_indices": torch.empty(R, **i32)}
     kc, vc = wl.key_cache, wl.value_cache
+    ks = vs = None
+    if wl.kv_scales is not None:
+        ks = torch.tensor([wl.kv_scales[0]], dtype=torch.float32, device=dev)
+        vs = torch.tensor([wl.kv_scales[1]], dtype=torch.float32, device=dev)
     out = torch.empty_like(wl.q)
     ws_bytes = pkv.attention_workspace_bytes(R, T, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                              wl.max_query_len, wl.max_seq_len, args.split_tokens,
@@ -241,14 +258,18 @@ def main():
                            num_blocks=wl.num_blocks, out=prep)
         if ev is not None:
             ev[1].record(stream)
-        pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"],
-                           block_size=wl.block_size)
+        if ks is None:
+            pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"],
+                               block_size=wl.block_size)
+        else:
+            pkv.kv_cache_write_fp8(wl.key, wl.value, kc, vc, prep["slot_mapping"], ks, vs,
+                                   block_size=wl.block_size)
         if ev is not None:
             ev[2].record(stream)
         pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
                             max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
                             scale=wl.scale, out=out, split_tokens=args.split_tokens,
-                            workspace=ws)
+                            workspace=ws, k_scale=ks, v_scale=vs)
         if ev is not None:
             ev[3].record(stream)
 
@@ -298,7 +319,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = measured_traffic(f"w{args.workload}_{args.rows}_split{args.split_tokens}")
+    key = f"w{args.workload}_{args.rows}_split{args.split_tokens}"
+    roof["traffic"] = measured_traffic(key + ("_fp8" if args.kv_dtype == "fp8" else ""))
     roof["kernel"] = "paged_attention_varlen (plan + attn_main + reduce), HIP events"
     roof["algorithmic_bytes"] = work["bytes_unique"]
     roof["algorithmic_flops"] = flops
@@ -316,13 +338,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "dtype": ("bf16" if wl.dtype == torch.bfloat16 else "f32") +
+                 ("+fp8kv" if args.kv_dtype == "fp8" else ""),
         "data": "synthetic (seeded N(0,1) K/V/Q, random block placement)",
         "config": {"workload": workloads.CONFIG_NAMES[args.workload], "num_reqs": R,
                    "num_tokens": T, "context_tokens": work["context_tokens"],
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "seed": wl.seed,
-                   "split_tokens": args.split_tokens, "rows": args.rows},
+                   "split_tokens": args.split_tokens, "rows": args.rows,
+                   "kv_dtype": args.kv_dtype},
         "phases_ms": {"prepare": round(t_prep, 4), "kv_write": round(t_write, 4),
                       "attention": round(t_attn, 4)},
         "context_tokens_per_s": round(work["context_tokens"] / (ms_step / 1e3), 1),

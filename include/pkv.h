@@ -14,7 +14,8 @@
  *   pkv_paged_attention_varlen causal attention of every query row of the
  *                              step (prefill chunks and single-token decodes
  *                              alike, in one launch) over its request's
- *                              context, read through the block table.
+ *                              context, read through the block table;
+ *   pkv_paged_attention_varlen_fp8  the same over FP8 pools.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -271,6 +272,27 @@ pkv_status pkv_paged_attention_varlen(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     float scale, pkv_dtype dtype, int32_t split_tokens, void* workspace,
     size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attention_varlen_fp8 -- pkv_paged_attention_varlen over FP8 E4M3
+ * pools written by pkv_kv_cache_write_fp8 ("How vLLM Works Internally: A Deep
+ * Dive", "FP8 KV Cache").  Every K element reads as its E4M3 value times
+ * *k_scale and every V element as its E4M3 value times *v_scale; the result is
+ * then exactly what pkv_paged_attention_varlen defines over those values.
+ * q and out are bf16 (the dtype is implied); the pools use the FP8 layouts of
+ * pkv_kv_cache_write_fp8; k_scale, v_scale are device float32 scalars,
+ * positive and finite (preconditions).  The other arguments, the workspace
+ * (same size as for bf16) and the errors are those of
+ * pkv_paged_attention_varlen; null scales give PKV_ERR_INVALID_ARG.
+ */
+pkv_status pkv_paged_attention_varlen_fp8(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, const float* k_scale, const float* v_scale, int32_t split_tokens,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 EXPORTS = ("pkv_status_string", "pkv_prepare_inputs", "pkv_kv_cache_write",
            "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
-           "pkv_paged_attention_varlen")
+           "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8")
 
 
 class PkvError(RuntimeError):
@@ -58,6 +58,10 @@ def load() -> ctypes.CDLL:
                                                i32, i32, i32, i32, i32, i32, f32, ctypes.c_int,
                                                i32, P, sz, P]
     lib.pkv_paged_attention_varlen.restype = ctypes.c_int
+    lib.pkv_paged_attention_varlen_fp8.argtypes = [P, i64, P, P, i64, P, i64, P, P, P, i64, i32,
+                                                   i32, i32, i32, i32, i32, i32, i32, f32, P, P,
+                                                   i32, P, sz, P]
+    lib.pkv_paged_attention_varlen_fp8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -171,10 +175,18 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                     query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
                     block_table: torch.Tensor, *, max_query_len: int, max_seq_len: int,
                     scale: float | None = None, out: torch.Tensor | None = None,
-                    split_tokens: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """pkv_paged_attention_varlen.  q: [T, Hq, d]; pools: K [nb, Hkv, 16, d], V [nb, Hkv, d, 16]."""
+                    split_tokens: int = 0, workspace: torch.Tensor | None = None,
+                    k_scale: torch.Tensor | None = None,
+                    v_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """pkv_paged_attention_varlen (or _fp8 when k_scale / v_scale are given).
+    q: [T, Hq, d]; 16-bit pools: K [nb, Hkv, 16, d], V [nb, Hkv, d, 16]; FP8
+    pools (uint8): K [nb, Hkv, 16, d], V [nb, Hkv, d * 16]; scales: one-element
+    float32 device tensors."""
     T, Hq, d = q.shape
     nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    fp8 = k_scale is not None
+    if fp8:
+        assert v_scale is not None and key_cache.dtype == torch.uint8
     R = int(seq_lens.shape[0])
     assert q.stride(2) == 1 and q.stride(1) == d
     assert key_cache.is_contiguous() and value_cache.is_contiguous()
@@ -189,13 +201,22 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, name="workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args_head = (_dev(q, name="q"), q.stride(0),
+                 _dev(key_cache, torch.uint8 if fp8 else q.dtype, "key_cache"),
+                 _dev(value_cache, torch.uint8 if fp8 else q.dtype, "value_cache"), nb,
+                 _dev(out, q.dtype, "out"), out.stride(0),
+                 _dev(query_start_loc, torch.int32, "query_start_loc"),
+                 _dev(seq_lens, torch.int32, "seq_lens"),
+                 _dev(block_table, torch.int32, "block_table"), block_table.stride(0), R, T,
+                 int(max_query_len), int(max_seq_len), Hq, Hkv, d, bs, float(scale))
+    if fp8:
+        st = load().pkv_paged_attention_varlen_fp8(
+            *args_head, _dev(k_scale, torch.float32, "k_scale"),
+            _dev(v_scale, torch.float32, "v_scale"), int(split_tokens), ws_ptr, ws_bytes,
+            _stream(q.device))
+        _check(st, "pkv_paged_attention_varlen_fp8")
+        return out
     st = load().pkv_paged_attention_varlen(
-        _dev(q, name="q"), q.stride(0), _dev(key_cache, q.dtype, "key_cache"),
-        _dev(value_cache, q.dtype, "value_cache"), nb, _dev(out, q.dtype, "out"), out.stride(0),
-        _dev(query_start_loc, torch.int32, "query_start_loc"),
-        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_table, torch.int32, "block_table"),
-        block_table.stride(0), R, T, int(max_query_len), int(max_seq_len), Hq, Hkv, d, bs,
-        float(scale), _dtype_code(q.dtype), int(split_tokens), ws_ptr, ws_bytes,
-        _stream(q.device))
+        *args_head, _dtype_code(q.dtype), int(split_tokens), ws_ptr, ws_bytes, _stream(q.device))
     _check(st, "pkv_paged_attention_varlen")
     return out

@@ -116,14 +116,17 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
   return plan.total_bytes;
 }
 
-pkv_status pkv_paged_attention_varlen(
+}  // extern "C"
+
+static pkv_status attention_call(
     const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
     int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
     const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
     int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    float scale, pkv_dtype dtype, int32_t split_tokens, void* workspace,
-    size_t workspace_bytes, void* stream) {
+    float scale, pkv_dtype dtype, const float* k_scale, const float* v_scale,
+    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool kv8 = k_scale != nullptr;
   if (num_reqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0 ||
       num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
       split_tokens < 0 || split_tokens % 32 != 0)
@@ -142,6 +145,9 @@ pkv_status pkv_paged_attention_varlen(
   if (plan.max_items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!q || !key_cache || !value_cache || !out || !query_start_loc || !seq_lens || !block_table)
+    return PKV_ERR_INVALID_ARG;
+  if (kv8 && (!v_scale || (reinterpret_cast<uintptr_t>(k_scale) & 3) != 0 ||
+              (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0))
     return PKV_ERR_INVALID_ARG;
   const int64_t row = (int64_t)num_q_heads * head_dim;
   const int32_t esz = dtype == PKV_BF16 ? 2 : 4;
@@ -173,9 +179,46 @@ pkv_status pkv_paged_attention_varlen(
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.scale = scale;
+  a.k_scale = kv8 ? k_scale : nullptr;
+  a.v_scale = kv8 ? v_scale : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == PKV_BF16) return launch_status(pkv::launch_attention_bf16(a, plan, workspace, s));
+  if (dtype == PKV_BF16)
+    return launch_status(pkv::launch_attention_bf16(a, plan, workspace, kv8, s));
   return launch_status(pkv::launch_attention_f32(a, s));
+}
+
+
+extern "C" {
+
+pkv_status pkv_paged_attention_varlen(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, int32_t split_tokens, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return attention_call(q, q_row_stride, key_cache, value_cache, num_blocks, out, out_row_stride,
+                        query_start_loc, seq_lens, block_table, bt_row_stride, num_reqs,
+                        num_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads,
+                        head_dim, block_size, scale, dtype, nullptr, nullptr, split_tokens,
+                        workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_varlen_fp8(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, const float* k_scale, const float* v_scale, int32_t split_tokens,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_scale || !v_scale) return PKV_ERR_INVALID_ARG;
+  return attention_call(q, q_row_stride, key_cache, value_cache, num_blocks, out, out_row_stride,
+                        query_start_loc, seq_lens, block_table, bt_row_stride, num_reqs,
+                        num_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads,
+                        head_dim, block_size, scale, PKV_BF16, k_scale, v_scale, split_tokens,
+                        workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -564,6 +564,191 @@ __device__ __attribute__((always_inline)) inline void walk_steps(
 }
 
 // ---------------------------------------------------------------------------
+// FP8 E4M3 pools: the decode walk
+// ---------------------------------------------------------------------------
+//
+// An FP8 run of one (block, kv head) is 16 * D bytes.  K is token-major; a
+// lane's 16-byte load of token n at dims 64t + 16g .. + 15 holds the A
+// operands of QK k-steps 2t (its first 8 bytes) and 2t + 1 (the last 8): the
+// contraction over dims may run in any order as long as Q follows the same
+// one.  V runs are laid out [dim / 64][token / 4][dim % 16][(dim / 16) % 4]
+// [token % 4], so one 16-byte load of lane (n, g) holds tokens 4g..4g+3 of
+// dims 64 dq + 16 dt + n for four 16-dim tiles dt: the V^T operand runs of
+// four PV MFMAs.  Codes widen exactly to bf16; k_scale is folded into the
+// softmax scale and v_scale into the output.
+
+template <int D>
+struct Geometry8 {
+  static constexpr int kHeadBytes = kBlock * D;  // one (block, kv head) run
+  static constexpr int KL = D / 64;               // 16-byte K loads per token row
+  static constexpr int VL = D / 64;               // 16-byte V loads per lane and block
+};
+
+template <int D>
+struct StepLoads8 {
+  u32x4 k0[Geometry8<D>::KL], k1[Geometry8<D>::KL];
+  u32x4 v0[Geometry8<D>::VL], v1[Geometry8<D>::VL];
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (bytes of a, then of b) as eight bf16 values (exact).
+__device__ inline bf16x8 fp8x8_to_bf16(unsigned a, unsigned b) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int D>
+__device__ inline rsrc_t run_rsrc8(const char* run, bool valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(run), 0,
+                                           valid ? (int)Geometry8<D>::kHeadBytes : 0, kRsrcWord3);
+}
+
+template <int D>
+__device__ inline StepRsrc make_step8(const AttnArgs& a, int b0, int b1, const char* kbase,
+                                      const char* vbase) {
+  StepRsrc r;
+  r.ok0 = b0 >= 0 && b0 < a.num_blocks;
+  r.ok1 = b1 >= 0 && b1 < a.num_blocks;
+  const int64_t stride = (int64_t)a.num_kv_heads * Geometry8<D>::kHeadBytes;
+  const int64_t o0 = (r.ok0 ? (int64_t)b0 : 0) * stride;
+  const int64_t o1 = (r.ok1 ? (int64_t)b1 : 0) * stride;
+  r.k0 = run_rsrc8<D>(kbase + o0, r.ok0);
+  r.k1 = run_rsrc8<D>(kbase + o1, r.ok1);
+  r.v0 = run_rsrc8<D>(vbase + o0, r.ok0);
+  r.v1 = run_rsrc8<D>(vbase + o1, r.ok1);
+  return r;
+}
+
+template <int D>
+__device__ inline void issue_step_loads8(StepLoads8<D>& ld, const StepRsrc& r, int k_lane,
+                                         int v_lane) {
+#pragma unroll
+  for (int t = 0; t < Geometry8<D>::KL; ++t) {
+    ld.k0[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + 64 * t, 0, kKvLoadPolicy);
+    ld.k1[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + 64 * t, 0, kKvLoadPolicy);
+  }
+#pragma unroll
+  for (int q = 0; q < Geometry8<D>::VL; ++q) {
+    ld.v0[q] = __builtin_amdgcn_raw_buffer_load_b128(r.v0, v_lane + 1024 * q, 0, kKvLoadPolicy);
+    ld.v1[q] = __builtin_amdgcn_raw_buffer_load_b128(r.v1, v_lane + 1024 * q, 0, kKvLoadPolicy);
+  }
+}
+
+// tile_step over FP8 loads: qf[s] must hold dims 64(s / 2) + 16g + 8(s % 2)
+// .. + 7 of the lane's column.
+template <int D, bool MASK>
+__device__ inline void tile_step8(TileState<D>& st, const bf16x8* qf, const StepLoads8<D>& ld,
+                                  int kpos, int p_col, bool ok0, bool ok1, int seq_len,
+                                  float c2) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < Geometry8<D>::KL; ++t) {
+    s0 = mfma_bf16(fp8x8_to_bf16(ld.k0[t].x, ld.k0[t].y), qf[2 * t], s0);
+    s1 = mfma_bf16(fp8x8_to_bf16(ld.k1[t].x, ld.k1[t].y), qf[2 * t], s1);
+    s0 = mfma_bf16(fp8x8_to_bf16(ld.k0[t].z, ld.k0[t].w), qf[2 * t + 1], s0);
+    s1 = mfma_bf16(fp8x8_to_bf16(ld.k1[t].z, ld.k1[t].w), qf[2 * t + 1], s1);
+  }
+  unsigned keep0 = 0xFu, keep1 = 0xFu;
+  if (MASK) {
+    keep0 = 0u;
+    keep1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s0[i] = (ok0 && kpos + i <= p_col) ? s0[i] : -INFINITY;
+      s1[i] = (ok1 && kpos + 16 + i <= p_col) ? s1[i] : -INFINITY;
+      keep0 |= (ok0 && kpos + i < seq_len) ? (1u << i) : 0u;
+      keep1 |= (ok1 && kpos + 16 + i < seq_len) ? (1u << i) : 0u;
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                   fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+  mx = column_max(mx);
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2((st.m - m_use) * c2);
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = fast_exp2((s0[i] - m_use) * c2);
+    p[4 + i] = fast_exp2((s1[i] - m_use) * c2);
+  }
+  st.l = st.l * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+  st.m = m_new;
+  bf16x8 pf;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pf[i] = static_cast<__bf16>(p[i]);
+#pragma unroll
+  for (int q = 0; q < Geometry8<D>::VL; ++q) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      u32x2 lo = __builtin_bit_cast(u32x2, fp8x8_to_bf16(ld.v0[q][w], 0u).lo);
+      u32x2 hi = __builtin_bit_cast(u32x2, fp8x8_to_bf16(ld.v1[q][w], 0u).lo);
+      if (MASK) {
+        lo = keep_bf16x4(lo, keep0);
+        hi = keep_bf16x4(hi, keep1);
+      }
+      const int dt = 4 * q + w;
+      st.o[dt] *= alpha;
+      st.o[dt] = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pf,
+                           st.o[dt]);
+    }
+  }
+}
+
+// walk_steps over FP8 pools (same pipeline: loads of step s+1 in flight while
+// step s is computed).
+template <int D>
+__device__ __attribute__((always_inline)) inline void walk_steps8(
+    TileState<D>& st, const bf16x8 (&qf)[Geometry<D>::KS], int p_col, const AttnArgs& a,
+    table_t* bt, int nblk, int s_begin, int s_end, int p_unmasked, int seq_len,
+    const char* kbase, const char* vbase, float c2) {
+  if (s_begin >= s_end) return;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int k_lane = n * D + 16 * g;
+  const int v_lane = (16 * g + n) * 16;
+  const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
+  const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
+  const int lim_walk = min(lim, 2 * s_end);
+  auto ids_at = [&](int step) {
+    const int j0 = 2 * step, j1 = j0 + 1;
+    int b0 = bt[min(j0, last_col)];
+    int b1 = bt[min(j1, last_col)];
+    return int2{j0 < lim_walk ? b0 : -1, j1 < lim_walk ? b1 : -1};
+  };
+  auto compute = [&](const StepLoads8<D>& ld, const StepRsrc& sb, int step) {
+    const int kpos = step * 2 * kBlock + 4 * g;
+    const bool mask = (step * 2 * kBlock + 2 * kBlock - 1 > p_unmasked) || !sb.ok0 || !sb.ok1;
+    if (mask)
+      tile_step8<D, true>(st, qf, ld, kpos, p_col, sb.ok0, sb.ok1, seq_len, c2);
+    else
+      tile_step8<D, false>(st, qf, ld, kpos, p_col, true, true, seq_len, c2);
+  };
+  StepLoads8<D> A, B;
+  int2 ids = ids_at(s_begin);
+  StepRsrc sa = make_step8<D>(a, ids.x, ids.y, kbase, vbase), sbk;
+  issue_step_loads8<D>(A, sa, k_lane, v_lane);
+  ids = ids_at(s_begin + 1);
+  int step = s_begin;
+  while (true) {
+    sbk = make_step8<D>(a, ids.x, ids.y, kbase, vbase);
+    ids = ids_at(step + 2);
+    issue_step_loads8<D>(B, sbk, k_lane, v_lane);
+    compute(A, sa, step);
+    if (++step >= s_end) break;
+    sa = make_step8<D>(a, ids.x, ids.y, kbase, vbase);
+    ids = ids_at(step + 2);
+    issue_step_loads8<D>(A, sa, k_lane, v_lane);
+    compute(B, sbk, step);
+    if (++step >= s_end) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // decode item
 // ---------------------------------------------------------------------------
 
@@ -574,9 +759,11 @@ struct DecodeSmem {
   float o[kWaves][kPairsPerTile][D + 4];
 };
 
-template <int D>
-__device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kvh, int split,
-                           int nsplit, int max_splits, float* __restrict__ ml,
+// KV8: the pools hold FP8 E4M3 codes; c2 already carries k_scale and vs is
+// v_scale (1 for 16-bit pools).
+template <int D, bool KV8>
+__device__ void run_decode(const AttnArgs& a, int group, float c2, float vs, int r, int kvh,
+                           int split, int nsplit, int max_splits, float* __restrict__ ml,
                            float* __restrict__ opart, DecodeSmem<D>& sm) {
   using Geo = Geometry<D>;
   const int lane = threadIdx.x & 63;
@@ -599,7 +786,9 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
                        ((int64_t)(row0 + t) * a.q_stride + (int64_t)head * D) * 2;
 #pragma unroll
     for (int s = 0; s < Geo::KS; ++s) {
-      qf[0][s] = col_ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
+      // the FP8 K loads pair k-steps 2t and 2t+1 over dims 64t + 16g .. + 15
+      const int dim = KV8 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
+      qf[0][s] = col_ok ? ld_b128(qrow + dim * 2)
                         : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
   }
@@ -614,12 +803,18 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
   const int w_end = min(sp_end, w_begin + per_wave);
 
   table_t* bt = table_row(a.block_table, a.bt_stride, r);
-  const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
-  const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
+  const int64_t run = KV8 ? Geometry8<D>::kHeadBytes : Geo::kHeadBytes;
+  const char* kbase = static_cast<const char*>(a.key_cache) + kvh * run;
+  const char* vbase = static_cast<const char*>(a.value_cache) + kvh * run;
 
   TileState<D> st[1];
   tile_init(st[0]);
-  walk_steps<D, 1>(st, qf, p_col, a, bt, nblk, w_begin, w_end, L - q_len, L, kbase, vbase, c2);
+  if (KV8)
+    walk_steps8<D>(st[0], qf[0], p_col[0], a, bt, nblk, w_begin, w_end, L - q_len, L, kbase,
+                   vbase, c2);
+  else
+    walk_steps<D, 1>(st, qf, p_col, a, bt, nblk, w_begin, w_end, L - q_len, L, kbase, vbase,
+                     c2);
 
   // merge the four waves' states
   const float l_tot = column_sum(st[0].l);
@@ -654,6 +849,8 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, int r, int kv
 #pragma unroll
       for (int k = 0; k < kDimsPerThread; ++k) acc[k] += f * sm.o[w][cn][cd + k];
     }
+#pragma unroll
+    for (int k = 0; k < kDimsPerThread; ++k) acc[k] *= vs;
     const int tt = cn / group;
     const int hh = kvh * group + (cn - tt * group);
     if (nsplit == 1) {
@@ -924,9 +1121,14 @@ __device__ __attribute__((always_inline)) inline void prefill_step(
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D>
-__device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int kvh, int mtile,
-                            PrefillSmem<D>& sm) {
+// KV8: the pools hold FP8 E4M3 codes (c2 already carries k_scale, vs is
+// v_scale).  Each wave then copies its block's FP8 runs into a staging area
+// (the space of the second 16-bit buffer) and, once all waves have finished
+// the current step, widens them into the single 16-bit buffer in the layout
+// below: two barriers per step instead of one.
+template <int D, bool KV8>
+__device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, int r, int kvh,
+                            int mtile, PrefillSmem<D>& sm) {
   using Geo = Geometry<D>;
   using Lay = PrefillLayout<D>;
   constexpr int NT = kPrefillTilesPerWave;
@@ -976,9 +1178,10 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
                                    : 0;
 
   table_t* bt = table_row(a.block_table, a.bt_stride, r);
-  const char* kbase = static_cast<const char*>(a.key_cache) + kvh * Geo::kHeadBytes;
-  const char* vbase = static_cast<const char*>(a.value_cache) + kvh * Geo::kHeadBytes;
-  const int64_t blk_stride = (int64_t)a.num_kv_heads * Geo::kHeadBytes;
+  constexpr int64_t kRunBytes = KV8 ? Geometry8<D>::kHeadBytes : Geo::kHeadBytes;
+  const char* kbase = static_cast<const char*>(a.key_cache) + kvh * kRunBytes;
+  const char* vbase = static_cast<const char*>(a.value_cache) + kvh * kRunBytes;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * kRunBytes;
   const int nblk = L > 0 ? ceil_div(L, kBlock) : 0;
   const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
   const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
@@ -1001,10 +1204,33 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   // Issue this wave's copy of block `wave` of a step into LDS buffer `buf`.
   // Returns whether the block is readable (inside the context, id inside the
   // pool); a block that is not is not read at all.
+  // FP8 staging: wave w's K run at stage + 2w * kRun8, its V run after it,
+  // both copied verbatim (lane i of copy c fills bytes 1024c + 16i).
+  constexpr int kRun8 = Geometry8<D>::kHeadBytes;
+  static_assert(!KV8 || 8 * kRun8 <= Lay::kBytes, "FP8 stage must fit one 16-bit K area");
+  char* stage_k = sm.bytes + Lay::kOff1 + 2 * wave * kRun8;
+  char* stage_v = stage_k + kRun8;
   auto fetch = [&](int step, int buf) {
     const int j = 4 * step + wave;
     const int id = bt[min(j, last_col)];
     const bool ok = j < lim && step < nsteps && id >= 0 && id < a.num_blocks;
+    if (KV8) {
+      if (ok) {
+        const int64_t off = (int64_t)id * blk_stride;
+        const rsrc_t rk8 = run_rsrc8<D>(kbase + off, true);
+        const rsrc_t rv8 = run_rsrc8<D>(vbase + off, true);
+#pragma unroll
+        for (int c = 0; c < kRun8 / 1024; ++c) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk8, (lds_void*)(stage_k + c * 1024), 16,
+                                                   16 * lane + 1024 * c, 0, 0,
+                                                   kPrefillLoadPolicy);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv8, (lds_void*)(stage_v + c * 1024), 16,
+                                                   16 * lane + 1024 * c, 0, 0,
+                                                   kPrefillLoadPolicy);
+        }
+      }
+      return ok;
+    }
     if (ok) {
       const int64_t off = (int64_t)id * blk_stride;
       const rsrc_t rk_d = run_rsrc<D>(kbase + off, true);
@@ -1026,6 +1252,34 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   // and zero V tokens past the context in the last block (their weight is 0,
   // but the pool may hold NaN there and 0 * NaN would poison the sum).
   auto finish = [&](int step, int buf, bool ok) {
+    if (KV8) {  // widen this wave's staged FP8 runs into 16-bit buffer 0
+      char* kdst = sm.bytes + Lay::kOff0 + wave * Lay::kRun;
+      char* vdst = sm.bytes + Lay::vOff0 + wave * Lay::vRun;
+      if (lane == 0) sm.valid[0][wave] = ok ? 1 : 0;
+      const int tok0 = step * kPrefillStep + wave * kBlock;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (ok) {
+          // K: token lane & 15, dims 8(4q + (lane >> 4)) .. + 7
+          const u32x2 k8 = *reinterpret_cast<const u32x2*>(
+              stage_k + (lane & 15) * D + 8 * (4 * q + (lane >> 4)));
+          kv = __builtin_bit_cast(u32x4, fp8x8_to_bf16(k8.x, k8.y));
+          // V slot S: dim 16(S / 32) + S % 16, tokens 8c .. 8c+7 with c = (S / 16) % 2,
+          // held as token groups 2c and 2c+1 of the FP8 run
+          const int S = q * 64 + lane;
+          const int dim = 16 * (S >> 5) + (S & 15), c = (S >> 4) & 1;
+          const int base = ((dim >> 6) * 4 + 2 * c) * 256 + (dim & 15) * 16 + ((dim >> 4) & 3) * 4;
+          const unsigned w0 = *reinterpret_cast<const unsigned*>(stage_v + base);
+          const unsigned w1 = *reinterpret_cast<const unsigned*>(stage_v + base + 256);
+          vv = __builtin_bit_cast(u32x4, fp8x8_to_bf16(w0, w1));
+          if (tok0 + kBlock > L) vv = keep_below(vv, tok0 + 8 * c, L);
+        }
+        if (ok) *reinterpret_cast<u32x4*>(kdst + q * 1024 + 16 * lane) = kv;
+        *reinterpret_cast<u32x4*>(vdst + q * 1024 + 16 * lane) = vv;
+      }
+      return;
+    }
     char* vdst = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + wave * Lay::vRun;
     if (lane == 0) sm.valid[buf][wave] = ok ? 1 : 0;
     const int tok0 = step * kPrefillStep + wave * kBlock;  // first token of this block
@@ -1074,7 +1328,7 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
   }
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
+    const int buf = KV8 ? 0 : step & 1;
     const bool ok_next = fetch(step + 1, buf ^ 1);
     if (step * kPrefillStep <= p_hi) {
       const char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + k_rd;
@@ -1089,6 +1343,7 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
       prefill_step<D, NT>(o, lacc, mref, has_ref, qf, kb, vb, mask, valid, step, p_col, ones);
     }
     wait_copies();
+    if (KV8) __syncthreads();  // the single 16-bit buffer is read by every wave
     finish(step + 1, buf ^ 1, ok_next);
     __syncthreads();
   }
@@ -1101,7 +1356,7 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, int r, int k
     if (P < pairs) {
       const int t = P / group;
       const int head = kvh * group + (P - t * group);
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? vs / l_tot : 0.f;
       char* dst = static_cast<char*>(a.out) +
                   ((int64_t)(row0 + t) * a.out_stride + (int64_t)head * D + 4 * g) * 2;
 #pragma unroll
@@ -1124,7 +1379,7 @@ union MainSmem {
 // Two workgroups per CU (2 waves per SIMD, <= 256 registers per lane): one
 // wave's softmax VALU work overlaps the other's MFMAs, and a decode item's
 // start-up latency overlaps the other workgroup's loads.
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_main_kernel(
     AttnArgs a, int32_t group, float c2, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items, int32_t max_splits, float* __restrict__ ml,
@@ -1132,10 +1387,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ MainSmem<D> sm;
   if ((int)blockIdx.x >= *n_items) return;
   const int4 it = items[blockIdx.x];
+  // FP8 pools: k_scale joins the softmax scale, v_scale the output
+  const float c2k = KV8 ? c2 * *a.k_scale : c2;
+  const float vs = KV8 ? *a.v_scale : 1.f;
   if (it.w < 0)
-    run_prefill<D>(a, group, c2, it.x, it.y, it.z, sm.pre);
+    run_prefill<D, KV8>(a, group, c2k, vs, it.x, it.y, it.z, sm.pre);
   else
-    run_decode<D>(a, group, c2, it.x, it.y, it.z, it.w, max_splits, ml, opart, sm.dec);
+    run_decode<D, KV8>(a, group, c2k, vs, it.x, it.y, it.z, it.w, max_splits, ml, opart,
+                       sm.dec);
 }
 
 // ---------------------------------------------------------------------------
@@ -1155,6 +1414,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a, int32_t gr
   if (pairs < 1 || pairs > kPairsPerTile) return;
   const int nsplit = num_splits(a.seq_lens[r], split_tokens, max_splits);
   if (nsplit <= 1) return;
+  if (a.k_scale != nullptr) c2 *= *a.k_scale;  // partial maxima are raw FP8 scores
   constexpr int kDimsPerThread = D / 16;
   const int cn = threadIdx.x >> 4;
   const int cd = (threadIdx.x & 15) * kDimsPerThread;
@@ -1266,7 +1526,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int32_t group)
   for (int k = 0; k < PER; ++k) out[lane + 64 * k] = o[k] * inv;
 }
 
-template <int D>
+template <int D, bool KV8>
 hipError_t launch_bf16_d(const AttnArgs& a, const AttnPlan& plan, void* workspace,
                          hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
@@ -1281,7 +1541,7 @@ hipError_t launch_bf16_d(const AttnArgs& a, const AttnPlan& plan, void* workspac
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (plan.max_items > 0) {
-    hipLaunchKernelGGL(attn_main_kernel<D>, dim3((unsigned)plan.max_items), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_main_kernel<D, KV8>), dim3((unsigned)plan.max_items), dim3(kThreads), 0,
                        stream, a, plan.group, c2, items, n_items, plan.max_splits, ml, opart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1350,10 +1610,14 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
 }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, const AttnPlan& plan, void* workspace,
-                                 hipStream_t stream) {
+                                 bool kv8, hipStream_t stream) {
   if (a.num_tokens == 0 || a.num_reqs == 0) return hipSuccess;
-  if (a.head_dim == 128) return launch_bf16_d<128>(a, plan, workspace, stream);
-  return launch_bf16_d<64>(a, plan, workspace, stream);
+  if (kv8) {
+    if (a.head_dim == 128) return launch_bf16_d<128, true>(a, plan, workspace, stream);
+    return launch_bf16_d<64, true>(a, plan, workspace, stream);
+  }
+  if (a.head_dim == 128) return launch_bf16_d<128, false>(a, plan, workspace, stream);
+  return launch_bf16_d<64, false>(a, plan, workspace, stream);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {

@@ -71,10 +71,13 @@ struct AttnArgs {
   int32_t num_kv_heads;
   int32_t head_dim;
   float scale;
+  const float* k_scale;  // FP8 pools: device scalars; null for 16-bit pools
+  const float* v_scale;
 };
 
+// bf16 queries; kv8 selects FP8 E4M3 pools (a.k_scale / a.v_scale set).
 hipError_t launch_attention_bf16(const AttnArgs& a, const AttnPlan& plan, void* workspace,
-                                 hipStream_t stream);
+                                 bool kv8, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace pkv

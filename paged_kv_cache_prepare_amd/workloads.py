@@ -25,6 +25,12 @@ Layouts (the library's interface, not part of the method): new rows are
 [T, H, d]; the K pool is [num_blocks, Hkv, block_size, d]; the V pool is
 [num_blocks, Hkv, d, block_size].
 
+FP8 pools (``to_fp8``): the same history as E4M3 codes of value / scale,
+converted by torch's float8_e4m3fn (after clamping to +-448; NaN poison stays
+NaN), as uint8 tensors: K [num_blocks, Hkv, 16, d] token-major, V
+[num_blocks, Hkv, d * 16] in the documented FP8 V order (per run: dim / 64,
+token / 4, dim % 16, (dim / 16) % 4, token % 4).
+
 The five named configurations are the shapes of the pages' workloads: a
 three-request step of the worked example ("Building the Batch", "How they are
 computed"), 13B- and 8B-shaped decode batches, one 5,000-token prompt chunk
@@ -63,6 +69,7 @@ class Workload:
     key_cache: torch.Tensor = None     # [nb, Hkv, bs, d]
     value_cache: torch.Tensor = None   # [nb, Hkv, d, bs]
     notes: dict = field(default_factory=dict)
+    kv_scales: tuple = None            # (k_scale, v_scale) when the pools hold FP8 codes
 
     @property
     def num_reqs(self) -> int:
@@ -192,6 +199,39 @@ def build(name: str, nst, nct, *, num_q_heads: int, num_kv_heads: int, head_dim:
     return wl
 
 
+def fp8_value_order(head_dim: int, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """For each byte of an FP8 V run, the flat index dim * block_size + token of
+    the element it holds (the documented FP8 V order)."""
+    assert block_size == 16 and head_dim % 64 == 0
+    order = np.empty(head_dim * block_size, np.int64)
+    for dim in range(head_dim):
+        for tok in range(block_size):
+            byte = ((((dim // 64) * 4 + tok // 4) * 16 + dim % 16) * 4 + (dim // 16) % 4) * 4 \
+                + tok % 4
+            order[byte] = dim * block_size + tok
+    return order
+
+
+def to_fp8(wl: Workload, k_scale: float, v_scale: float) -> Workload:
+    """The same step with FP8 pools: every history element as the E4M3 code of
+    value / scale (torch's float8_e4m3fn conversion).  New rows stay bf16."""
+    assert wl.dtype == torch.bfloat16
+    nb, H, bs, d = wl.key_cache.shape
+
+    def codes(x, scale):
+        return (x.float() / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    kc = codes(wl.key_cache, k_scale).contiguous()
+    order = torch.from_numpy(fp8_value_order(d, bs)).to(wl.value_cache.device)
+    vc = codes(wl.value_cache, v_scale).reshape(nb, H, d * bs)[:, :, order].contiguous()
+    out = Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
+    out.name = wl.name + "-fp8"
+    out.key_cache, out.value_cache = kc, vc
+    out.kv_scales = (float(np.float32(k_scale)), float(np.float32(v_scale)))
+    out.notes = dict(wl.notes)
+    return out
+
+
 def select(wl: Workload, reqs, name: str | None = None) -> Workload:
     """The sub-batch of requests ``reqs`` (in order) over the same block pools:
     their scheduled rows of Q/K/V, counts and block-table rows."""
@@ -209,7 +249,7 @@ def select(wl: Workload, reqs, name: str | None = None) -> Workload:
                    block_size=wl.block_size, dtype=wl.dtype, scale=wl.scale, seed=wl.seed,
                    q=wl.q[idx].contiguous(), key=wl.key[idx].contiguous(),
                    value=wl.value[idx].contiguous(), key_cache=wl.key_cache,
-                   value_cache=wl.value_cache, notes=dict(wl.notes))
+                   value_cache=wl.value_cache, notes=dict(wl.notes), kv_scales=wl.kv_scales)
     return sub
 
 

@@ -32,14 +32,29 @@ def gpu_prepare(wl, qsl_len=None):
     return out, bt
 
 
+def gpu_scales(wl):
+    """One-element float32 device tensors of an FP8 workload's scales (else None, None)."""
+    if wl.kv_scales is None:
+        return None, None
+    dev = wl.q.device
+    return (torch.tensor([wl.kv_scales[0]], dtype=torch.float32, device=dev),
+            torch.tensor([wl.kv_scales[1]], dtype=torch.float32, device=dev))
+
+
 def gpu_step(wl, split_tokens=0):
     """prepare -> kv_write -> attention on the GPU (pool copies are written)."""
     prep, bt = gpu_prepare(wl)
     kc, vc = wl.key_cache.clone(), wl.value_cache.clone()
-    pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"], block_size=wl.block_size)
+    ks, vs = gpu_scales(wl)
+    if ks is None:
+        pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"],
+                           block_size=wl.block_size)
+    else:
+        pkv.kv_cache_write_fp8(wl.key, wl.value, kc, vc, prep["slot_mapping"], ks, vs,
+                               block_size=wl.block_size)
     out = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
                               max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
-                              scale=wl.scale, split_tokens=split_tokens)
+                              scale=wl.scale, split_tokens=split_tokens, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     return prep, kc, vc, out
 
@@ -49,13 +64,21 @@ def oracle_step(wl, rows=None):
     prep = oracle.prepare(wl.num_scheduled_tokens, wl.num_computed_tokens, wl.block_table,
                           wl.block_size, wl.num_blocks)
     kc, vc = wl.key_cache.cpu().clone(), wl.value_cache.cpu().clone()
-    oracle.kv_write(wl.key.cpu(), wl.value.cpu(), kc, vc, prep["slot_mapping"], wl.block_size)
+    if wl.kv_scales is None:
+        oracle.kv_write(wl.key.cpu(), wl.value.cpu(), kc, vc, prep["slot_mapping"],
+                        wl.block_size)
+    else:
+        oracle.kv_write_fp8(wl.key.cpu(), wl.value.cpu(), kc, vc, prep["slot_mapping"],
+                            wl.block_size, *wl.kv_scales)
     ref = oracle.attention(wl.q.cpu(), kc, vc, prep["query_start_loc"], prep["seq_lens"],
-                           wl.block_table, wl.block_size, wl.scale, rows=rows)
+                           wl.block_table, wl.block_size, wl.scale, rows=rows,
+                           kv_scales=wl.kv_scales)
     return prep, kc, vc, ref
 
 
 def bits_view(t):
+    if t.element_size() == 1:
+        return t.view(torch.uint8)
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
