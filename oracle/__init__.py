@@ -94,6 +94,12 @@ def _load():
     lib.orc_fp8_decode.restype = f64
     lib.orc_fp8_encode.argtypes = [ctypes.c_float]
     lib.orc_fp8_encode.restype = ctypes.c_uint8
+    lib.orc_input_ids.argtypes = [P, i64, i32, P, P, i32, P, P, P, P, P]
+    lib.orc_input_ids.restype = ctypes.c_int
+    lib.orc_copy_blocks.argtypes = [P, P, i64, i64, P, i32]
+    lib.orc_copy_blocks.restype = ctypes.c_int
+    lib.orc_zero_blocks.argtypes = [P, P, i64, i64, P, i32]
+    lib.orc_zero_blocks.restype = ctypes.c_int
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -147,6 +153,50 @@ def prepare(num_scheduled_tokens, num_computed_tokens, block_table, block_size: 
         raise OracleError(rc, "prepare")
     assert n_out.value == T
     return out
+
+
+def input_ids(token_table, req_indices, positions, seq_lens, num_tokens_total) -> dict:
+    """Token ids of the flat rows and the discard mask; see ``orc_input_ids``.
+    ``token_table`` is int32 [R, row_width] (request r in row r)."""
+    table = _i32(token_table)
+    R = int(np.asarray(seq_lens).shape[0])
+    table = table.reshape(max(R, 1) if table.size else 0, -1) if table.ndim == 1 else table
+    ri, pos = _i32(req_indices), _i32(positions)
+    T = int(ri.shape[0])
+    out = {"token_indices": np.zeros(T, np.int64), "input_ids": np.zeros(T, np.int32),
+           "discard_request_mask": np.zeros(R, np.uint8)}
+    rc = _load().orc_input_ids(_ptr(table), table.shape[1], R, _ptr(ri), _ptr(pos), T,
+                               _ptr(_i32(seq_lens)), _ptr(_i32(num_tokens_total)),
+                               _ptr(out["token_indices"]), _ptr(out["input_ids"]),
+                               _ptr(out["discard_request_mask"]))
+    if rc != OK:
+        raise OracleError(rc, "input_ids")
+    return out
+
+
+def _block_bytes(pool) -> int:
+    import torch
+    if isinstance(pool, np.ndarray):
+        return pool[0].nbytes if pool.shape[0] else 1
+    return pool[0].numel() * pool.element_size() if pool.shape[0] else 1
+
+
+def copy_blocks(key_cache, value_cache, pairs) -> None:
+    """Whole-block copies src -> dst in both pools, in order; see ``orc_copy_blocks``."""
+    pr = _i32(pairs).reshape(-1, 2)
+    rc = _load().orc_copy_blocks(_ptr(key_cache), _ptr(value_cache), key_cache.shape[0],
+                                 _block_bytes(key_cache), _ptr(pr), pr.shape[0])
+    if rc != OK:
+        raise OracleError(rc, "copy_blocks")
+
+
+def zero_blocks(key_cache, value_cache, block_ids) -> None:
+    """Clear the listed blocks of both pools; see ``orc_zero_blocks``."""
+    ids = _i32(block_ids).reshape(-1)
+    rc = _load().orc_zero_blocks(_ptr(key_cache), _ptr(value_cache), key_cache.shape[0],
+                                 _block_bytes(key_cache), _ptr(ids), ids.shape[0])
+    if rc != OK:
+        raise OracleError(rc, "zero_blocks")
 
 
 def kv_write(key, value, key_cache, value_cache, slot_mapping, block_size: int) -> None:

@@ -22,6 +22,17 @@
  *                     softmax attention in fp64 ("How vLLM Works Internally:
  *                     A Deep Dive", "How the Kernel Works", its four steps;
  *                     "Inside vLLM...", Part 5, the block_table read loop).
+ *   orc_input_ids  -- token ids gathered from the per-request token table at
+ *                     positions + request * row width, and the mask of
+ *                     requests whose sampled token is discarded ("Building
+ *                     the Batch", "How they are computed"; "vLLM's Model
+ *                     Runner...", "The batch contains rows that must not be
+ *                     sampled").
+ *   orc_copy_blocks, orc_zero_blocks
+ *                  -- whole-block copy for copy-on-write ("How vLLM Works
+ *                     Internally: A Deep Dive", "Copy-on-Write for Beam
+ *                     Search", step 3) and clearing of newly allocated blocks
+ *                     ("Inside vLLM...", Part 2: new_block_ids_to_zero).
  *   orc_kv_write_fp8, orc_attention_kv
  *                  -- the same write and read with an FP8 cache: each stored
  *                     element is an FP8 E4M3 code of the value divided by a
@@ -116,6 +127,85 @@ int orc_prepare(const int32_t* nst, const int32_t* nct, const int32_t* block_tab
       if (phys < 0 || phys >= num_blocks) return ORC_ERR_RANGE;
       slot_mapping[i] = (int64_t)phys * block_size + pos % block_size;
     }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* input ids and discard mask                                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The token table holds one row of row_width (the longest sequence a request
+ * may reach) token ids per request of the step, request r in row r.  For
+ * every flat row i:
+ *   token_indices[i] = positions[i] + req_indices[i] * row_width
+ *   input_ids[i]     = token_table[token_indices[i]]   (the table read as flat)
+ * and for every request r:
+ *   discard[r] = 1 if seq_lens[r] < num_tokens_total[r] else 0
+ * (seq_lens = computed + scheduled tokens, num_tokens_total = the request's
+ * known token count: a request still short of it is mid-prefill, and the token
+ * sampled from its last row is thrown away).  Returns ORC_ERR_RANGE when a row's
+ * request is outside [0, num_reqs) or its position outside [0, row_width).
+ */
+int orc_input_ids(const int32_t* token_table, int64_t row_width, int32_t num_reqs,
+                  const int32_t* req_indices, const int32_t* positions, int32_t num_tokens,
+                  const int32_t* seq_lens, const int32_t* num_tokens_total,
+                  int64_t* token_indices, int32_t* input_ids, uint8_t* discard) {
+  if (num_reqs < 0 || num_tokens < 0 || row_width <= 0) return ORC_ERR_ARG;
+  if (num_tokens > 0 && (!token_table || !req_indices || !positions || !token_indices ||
+                         !input_ids))
+    return ORC_ERR_ARG;
+  if (num_reqs > 0 && (!seq_lens || !num_tokens_total || !discard)) return ORC_ERR_ARG;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int32_t r = req_indices[i], p = positions[i];
+    if (r < 0 || r >= num_reqs || p < 0 || p >= row_width) return ORC_ERR_RANGE;
+    token_indices[i] = (int64_t)p + (int64_t)r * row_width;
+    input_ids[i] = token_table[token_indices[i]];
+  }
+  for (int32_t r = 0; r < num_reqs; ++r) discard[r] = seq_lens[r] < num_tokens_total[r] ? 1 : 0;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* block copy and zeroing                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Every pool keeps a block as one contiguous run of block_bytes bytes (all kv
+ * heads of one block: num_kv_heads * block_size * head_dim elements, whatever
+ * the order inside), so both operations are plain byte moves.
+ *
+ * orc_copy_blocks: for each pair k, block pairs[2k+1] of both pools becomes a
+ * byte copy of block pairs[2k] (the pairs are applied in order).
+ * orc_zero_blocks: every byte of the listed blocks of both pools becomes 0.
+ * Both return ORC_ERR_RANGE for a block id outside [0, num_blocks).
+ */
+int orc_copy_blocks(uint8_t* key_cache, uint8_t* value_cache, int64_t num_blocks,
+                    int64_t block_bytes, const int32_t* pairs, int32_t num_pairs) {
+  if (num_blocks < 0 || block_bytes <= 0 || num_pairs < 0) return ORC_ERR_ARG;
+  if (num_pairs > 0 && (!key_cache || !value_cache || !pairs)) return ORC_ERR_ARG;
+  for (int32_t k = 0; k < num_pairs; ++k) {
+    const int64_t src = pairs[2 * k], dst = pairs[2 * k + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return ORC_ERR_RANGE;
+  }
+  for (int32_t k = 0; k < num_pairs; ++k) {
+    const int64_t src = pairs[2 * k], dst = pairs[2 * k + 1];
+    memmove(key_cache + dst * block_bytes, key_cache + src * block_bytes, (size_t)block_bytes);
+    memmove(value_cache + dst * block_bytes, value_cache + src * block_bytes, (size_t)block_bytes);
+  }
+  return ORC_OK;
+}
+
+int orc_zero_blocks(uint8_t* key_cache, uint8_t* value_cache, int64_t num_blocks,
+                    int64_t block_bytes, const int32_t* block_ids, int32_t num_ids) {
+  if (num_blocks < 0 || block_bytes <= 0 || num_ids < 0) return ORC_ERR_ARG;
+  if (num_ids > 0 && (!key_cache || !value_cache || !block_ids)) return ORC_ERR_ARG;
+  for (int32_t k = 0; k < num_ids; ++k)
+    if (block_ids[k] < 0 || block_ids[k] >= num_blocks) return ORC_ERR_RANGE;
+  for (int32_t k = 0; k < num_ids; ++k) {
+    memset(key_cache + (int64_t)block_ids[k] * block_bytes, 0, (size_t)block_bytes);
+    memset(value_cache + (int64_t)block_ids[k] * block_bytes, 0, (size_t)block_bytes);
   }
   return ORC_OK;
 }

@@ -52,6 +52,14 @@ MUTANTS = {
                                           "(float)orc_load(key, src_k, dtype) * k_scale;"),
     "fp8 read ignores the value scale": ("phys, g, off, c, num_kv_heads, block_size, head_dim)]) * v_scale;",
                                          "phys, g, off, c, num_kv_heads, block_size, head_dim)]);"),
+    "token index uses position as the row": ("token_indices[i] = (int64_t)p + (int64_t)r * row_width;",
+                                             "token_indices[i] = (int64_t)r + (int64_t)p * row_width;"),
+    "discard mask keeps finished requests": ("discard[r] = seq_lens[r] < num_tokens_total[r] ? 1 : 0;",
+                                            "discard[r] = seq_lens[r] <= num_tokens_total[r] ? 1 : 0;"),
+    "block copy reversed": ("memmove(key_cache + dst * block_bytes, key_cache + src * block_bytes, (size_t)block_bytes);",
+                            "memmove(key_cache + src * block_bytes, key_cache + dst * block_bytes, (size_t)block_bytes);"),
+    "zeroing skips the value pool": ("memset(value_cache + (int64_t)block_ids[k] * block_bytes, 0, (size_t)block_bytes);",
+                                     "(void)0;"),
     "fp8 value layout collides": ("* 4 + (dim / 16) % 4) * 4 + tok % 4;", "* 4 + (dim / 32) % 4) * 4 + tok % 4;"),
 }
 

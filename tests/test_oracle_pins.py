@@ -625,3 +625,108 @@ def test_fp8_write_rejects_bad_arguments():
             oracle.kv_write_fp8(key, value, kc, vc, slots, 16, ks, 1.0)
     with pytest.raises(oracle.OracleError):
         oracle.kv_write_fp8(key, value, kc, vc, np.array([3, 3, -1, 4, 5, 6]), 16, 1.0, 1.0)
+
+
+# ---------------------------------------------------------------------------
+# input ids and the discard mask ("Building the Batch", "How they are
+# computed"; "vLLM's Model Runner...", "The batch contains rows that must
+# not be sampled")
+# ---------------------------------------------------------------------------
+
+def test_input_ids_token_indices_worked_example(golden):
+    g = golden["token_indices_example"]
+    M = 1000
+    table = np.arange(3 * M, dtype=np.int32).reshape(3, M) * 7 + 5
+    out = oracle.input_ids(table, g["req_indices"], g["positions"], [2, 5, 3], [2, 5, 3])
+    want = [a * M + b for a, b in g["token_indices_in_units_of_M"]]
+    assert out["token_indices"].tolist() == want
+    assert out["input_ids"].tolist() == [int(table.reshape(-1)[k]) for k in want]
+
+
+def test_discard_mask_worked_example(golden):
+    g = golden["discard_mask_example"]
+    nst, nct = g["num_scheduled_tokens"], g["num_computed_tokens"]
+    prep = oracle.prepare(nst, nct, _table([[0] * 7, [1], [2] * 3]), block_size=16,
+                          num_blocks=3)
+    table = np.zeros((3, 700), np.int32)
+    out = oracle.input_ids(table, prep["req_indices"], prep["positions"], prep["seq_lens"],
+                           g["num_tokens_total"])
+    assert out["discard_request_mask"].astype(bool).tolist() == g["discard_request_mask"]
+
+
+def test_input_ids_gather_random_batches():
+    rng = np.random.default_rng(21)
+    for _ in range(20):
+        R = int(rng.integers(1, 12))
+        M = int(rng.integers(64, 300))
+        nst = rng.integers(1, 20, R)
+        nct = rng.integers(0, M - 20, R)
+        total = nct + nst + rng.integers(-1, 5, R)  # some requests still mid-prompt
+        table = rng.integers(0, 50000, (R, M)).astype(np.int32)
+        bt = np.zeros((R, -(-M // 16)), np.int32)
+        prep = oracle.prepare(nst, nct, bt, block_size=16, num_blocks=1)
+        out = oracle.input_ids(table, prep["req_indices"], prep["positions"], prep["seq_lens"],
+                               total)
+        i = 0
+        for r in range(R):  # brute force: the t-th new token of r sits at nct + t of row r
+            for t in range(int(nst[r])):
+                assert out["input_ids"][i] == table[r, nct[r] + t]
+                i += 1
+        assert out["discard_request_mask"].tolist() == [int(nct[r] + nst[r] < total[r])
+                                                        for r in range(R)]
+
+
+def test_input_ids_rejects_positions_outside_the_table():
+    with pytest.raises(oracle.OracleError):
+        oracle.input_ids(np.zeros((2, 8), np.int32), [0, 1], [3, 8], [4, 9], [4, 9])
+    with pytest.raises(oracle.OracleError):
+        oracle.input_ids(np.zeros((2, 8), np.int32), [0, 2], [3, 1], [4, 2], [4, 2])
+
+
+# ---------------------------------------------------------------------------
+# block copy-on-write and zeroing ("How vLLM Works Internally: A Deep Dive",
+# "Copy-on-Write for Beam Search"; "Inside vLLM...", Part 2,
+# new_block_ids_to_zero)
+# ---------------------------------------------------------------------------
+
+def test_copy_and_zero_blocks_post_state():
+    rng = np.random.default_rng(2)
+    kc = rng.integers(0, 256, (9, 2, 16, 64), dtype=np.uint8)
+    vc = rng.integers(0, 256, (9, 2, 64, 16), dtype=np.uint8)
+    k0, v0 = kc.copy(), vc.copy()
+    oracle.copy_blocks(kc, vc, [[3, 7], [1, 0]])
+    assert np.array_equal(kc[7], k0[3]) and np.array_equal(vc[7], v0[3])
+    assert np.array_equal(kc[0], k0[1]) and np.array_equal(vc[0], v0[1])
+    for b in (1, 2, 3, 4, 5, 6, 8):
+        assert np.array_equal(kc[b], k0[b]) and np.array_equal(vc[b], v0[b])
+    oracle.zero_blocks(kc, vc, [2, 8])
+    assert not kc[2].any() and not vc[2].any() and not kc[8].any() and not vc[8].any()
+    assert np.array_equal(kc[4], k0[4]) and np.array_equal(vc[5], v0[5])
+    with pytest.raises(oracle.OracleError):
+        oracle.copy_blocks(kc, vc, [[0, 9]])
+    with pytest.raises(oracle.OracleError):
+        oracle.zero_blocks(kc, vc, [-1])
+
+
+def test_copy_on_write_keeps_the_other_beam_intact():
+    """Two beams share block 0 (positions 0..15) and diverge: beam 1 copies it
+    to block 2, points its table there and overwrites its last slot.  Beam 0's
+    attention is unchanged; beam 1 equals attention over an unshared pool that
+    holds the same rows."""
+    g = torch.Generator().manual_seed(4)
+    H, d, bs = 2, 64, 16
+    kc = torch.randn(4, H, bs, d, generator=g).to(torch.bfloat16)
+    vc = torch.randn(4, H, d, bs, generator=g).to(torch.bfloat16)
+    q = torch.randn(2, 4, d, generator=g).to(torch.bfloat16)
+    new_k = torch.randn(1, H, d, generator=g).to(torch.bfloat16)
+    new_v = torch.randn(1, H, d, generator=g).to(torch.bfloat16)
+    qsl, sl = [0, 1, 2], [16, 16]
+    before = oracle.attention(q, kc, vc, qsl, sl, [[0], [0]], bs, 0.125)
+    oracle.copy_blocks(kc, vc, [[0, 2]])
+    oracle.kv_write(new_k, new_v, kc, vc, [2 * bs + 15], bs)  # beam 1 writes its own copy
+    after = oracle.attention(q, kc, vc, qsl, sl, [[0], [2]], bs, 0.125)
+    assert np.array_equal(after[0], before[0])
+    fresh_k, fresh_v = kc[[0]].clone(), vc[[0]].clone()
+    oracle.kv_write(new_k, new_v, fresh_k, fresh_v, [15], bs)
+    alone = oracle.attention(q[1:], fresh_k, fresh_v, [0, 1], [16], [[0]], bs, 0.125)
+    assert np.array_equal(after[1], alone[0])
