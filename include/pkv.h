@@ -7,6 +7,9 @@
  *
  *   pkv_prepare_inputs         flat-batch index tensors from the scheduler's
  *                              per-request token counts and block tables;
+ *   pkv_prepare_input_ids      the step's input token ids gathered from the
+ *                              per-request token table, and the mask of
+ *                              requests whose sampled token is discarded;
  *   pkv_kv_cache_write         each new token's K and V rows into the block
  *                              pool at its slot;
  *   pkv_kv_cache_write_fp8     the same into an FP8 E4M3 pool with a scale
@@ -15,7 +18,11 @@
  *                              step (prefill chunks and single-token decodes
  *                              alike, in one launch) over its request's
  *                              context, read through the block table;
- *   pkv_paged_attention_varlen_fp8  the same over FP8 pools.
+ *   pkv_paged_attention_varlen_fp8  the same over FP8 pools;
+ *   pkv_copy_blocks            whole-block copies in both pools (copy-on-write
+ *                              of a shared block);
+ *   pkv_zero_blocks            whole-block clears in both pools (freshly
+ *                              allocated blocks).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -114,6 +121,45 @@ pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
                               int32_t* req_indices, int32_t* positions, int64_t* slot_mapping,
                               int32_t* query_start_loc, int32_t* seq_lens,
                               int32_t* logits_indices, void* stream);
+
+/*
+ * pkv_prepare_input_ids -- the step's input token ids and discard mask.
+ *
+ * Follows "Building the Batch", "How they are computed" (request r's tokens
+ * are row r of a table of row_width columns, so its token at position p is
+ * element r * row_width + p of the table read flat) and "vLLM's Model Runner
+ * -- the Persistent Batch, in Source", "The batch contains rows that must not
+ * be sampled" (a request still short of its known token count after this
+ * pass is mid-prefill; its sampled token is dropped).  For every flat row i
+ * with r = req_indices[i], p = positions[i]:
+ *   token_indices[i] = r * row_width + p
+ *   input_ids[i]     = token_table[token_indices[i]]
+ * and for every request r:
+ *   discard_request_mask[r] = seq_lens[r] < num_tokens_total[r] ? 1 : 0
+ * req_indices, positions and seq_lens are the outputs of pkv_prepare_inputs
+ * for the same step (enqueue that call first).
+ *
+ * Arguments (device pointers unless stated):
+ *   token_table     int32 [num_reqs or more][row_width], row r = request r
+ *   row_width       host, >= 1, the longest sequence a request may reach
+ *   num_reqs        host, >= 0;  num_tokens host, >= 0
+ *   req_indices, positions  int32 [num_tokens]
+ *   seq_lens, num_tokens_total  int32 [num_reqs]
+ *   token_indices   int64 [num_tokens] (out), or NULL when not wanted
+ *   input_ids       int32 [num_tokens] (out)
+ *   discard_request_mask  uint8 [num_reqs] (out), 0 or 1
+ * Device-data behaviour: a row with r outside [0, num_reqs) or p outside
+ * [0, row_width) (padding rows from pkv_prepare_inputs have -1 in both) gets
+ * token_indices = -1 and input_ids = -1; nothing outside the table is read.
+ * Errors: PKV_ERR_INVALID_ARG for negative sizes, row_width < 1, null
+ * pointers to non-empty arrays; PKV_ERR_LAUNCH.
+ */
+pkv_status pkv_prepare_input_ids(const int32_t* token_table, int64_t row_width,
+                                 int32_t num_reqs, const int32_t* req_indices,
+                                 const int32_t* positions, int32_t num_tokens,
+                                 const int32_t* seq_lens, const int32_t* num_tokens_total,
+                                 int64_t* token_indices, int32_t* input_ids,
+                                 uint8_t* discard_request_mask, void* stream);
 
 /*
  * pkv_kv_cache_write -- scatter this step's K and V rows into the block pool.
@@ -293,6 +339,56 @@ pkv_status pkv_paged_attention_varlen_fp8(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     float scale, const float* k_scale, const float* v_scale, int32_t split_tokens,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_copy_blocks -- copy-on-write of whole blocks, both pools at once.
+ *
+ * Follows "How vLLM Works Internally: A Deep Dive", "Copy-on-Write for Beam
+ * Search": before a beam writes into a block that other beams still share,
+ * the block's contents move to a newly allocated block that the beam's table
+ * then points to.  For every pair k, with (src, dst) = (block_pairs[2k],
+ * block_pairs[2k+1]), every byte of block dst in the K pool becomes the byte
+ * of block src in the K pool, and likewise in the V pool.  A block is the
+ * contiguous run of block_bytes bytes at offset id * block_bytes of a pool,
+ * which holds for every pool layout of this library (bf16, float32 and FP8
+ * alike): block_bytes = num_kv_heads * block_size * head_dim * element size.
+ *
+ * Arguments (device pointers unless stated):
+ *   key_cache, value_cache  the two pools, num_blocks blocks each, 16-byte
+ *                   aligned
+ *   num_blocks      host, >= 0;  block_bytes host, >= 16, a multiple of 16
+ *   block_pairs     int32 [num_pairs][2]: (source, destination)
+ *   num_pairs       host, >= 0
+ * Device-data preconditions: the destinations are distinct and none is also
+ * a source (a copy-on-write target is a freshly allocated block); sources may
+ * repeat (one block forked to several beams).  The copies then do not
+ * interact, and the result equals applying the pairs one after another.  A
+ * pair with an id outside [0, num_blocks) is skipped.
+ * Errors: PKV_ERR_INVALID_ARG for negative sizes, block_bytes < 16, null
+ * pointers when num_pairs > 0; PKV_ERR_UNSUPPORTED for block_bytes not a
+ * multiple of 16, unaligned pools, or more than 2^24 - 1 workgroups
+ * (2 * ceil(block_bytes / 16384) per pair); PKV_ERR_LAUNCH.
+ */
+pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                           int64_t block_bytes, const int32_t* block_pairs, int32_t num_pairs,
+                           void* stream);
+
+/*
+ * pkv_zero_blocks -- clear whole blocks in both pools.
+ *
+ * Follows "Inside vLLM: Following One Request from the API to GPU
+ * Execution", Part 2 (new_block_ids_to_zero): blocks handed to a request for
+ * the first time are cleared before the forward pass, so bytes left by an
+ * earlier owner (NaNs included) never reach attention.  Every byte of every
+ * listed block becomes 0 in both pools (0 is +0.0 in bf16, float32 and E4M3).
+ * Arguments and errors as for pkv_copy_blocks, with block_ids int32
+ * [num_ids] in place of the pairs; ids may repeat; an id outside
+ * [0, num_blocks) is skipped.  Kernel stores only (no memset node), so the
+ * call may be captured in a HIP graph.
+ */
+pkv_status pkv_zero_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                           int64_t block_bytes, const int32_t* block_ids, int32_t num_ids,
+                           void* stream);
 
 #ifdef __cplusplus
 }

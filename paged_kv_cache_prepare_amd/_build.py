@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
-SOURCES = ["api.hip", "prepare.hip", "kv_write.hip", "attention.hip"]
+SOURCES = ["api.hip", "prepare.hip", "kv_write.hip", "block_ops.hip", "attention.hip"]
 # Per-file flags.  The attention kernels never feed a NaN into a max or a sum
 # (masked scores are selected away first), so max operations need no NaN
 # canonicalisation.

@@ -17,9 +17,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-EXPORTS = ("pkv_status_string", "pkv_prepare_inputs", "pkv_kv_cache_write",
-           "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
-           "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8")
+EXPORTS = ("pkv_status_string", "pkv_prepare_inputs", "pkv_prepare_input_ids",
+           "pkv_kv_cache_write", "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
+           "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8", "pkv_copy_blocks",
+           "pkv_zero_blocks")
 
 
 class PkvError(RuntimeError):
@@ -45,6 +46,12 @@ def load() -> ctypes.CDLL:
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_prepare_inputs.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P, P, P, P, P]
     lib.pkv_prepare_inputs.restype = ctypes.c_int
+    lib.pkv_prepare_input_ids.argtypes = [P, i64, i32, P, P, i32, P, P, P, P, P, P]
+    lib.pkv_prepare_input_ids.restype = ctypes.c_int
+    lib.pkv_copy_blocks.argtypes = [P, P, i64, i64, P, i32, P]
+    lib.pkv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_zero_blocks.argtypes = [P, P, i64, i64, P, i32, P]
+    lib.pkv_zero_blocks.restype = ctypes.c_int
     lib.pkv_kv_cache_write.argtypes = [P, P, i64, i64, P, P, i64, P, i32, i32, i32, i32,
                                        ctypes.c_int, P]
     lib.pkv_kv_cache_write.restype = ctypes.c_int
@@ -125,6 +132,68 @@ def prepare_inputs(num_scheduled_tokens: torch.Tensor, num_computed_tokens: torc
         _stream(dev))
     _check(st, "pkv_prepare_inputs")
     return out
+
+
+def prepare_input_ids(token_table: torch.Tensor, req_indices: torch.Tensor,
+                      positions: torch.Tensor, seq_lens: torch.Tensor,
+                      num_tokens_total: torch.Tensor, *, with_token_indices: bool = False,
+                      out: dict | None = None) -> dict:
+    """pkv_prepare_input_ids.  token_table: int32 [rows >= num_reqs, row_width]
+    with contiguous rows; req_indices / positions / seq_lens as produced by
+    prepare_inputs; num_tokens_total: int32 [num_reqs]."""
+    T, R = int(req_indices.shape[0]), int(seq_lens.shape[0])
+    assert token_table.dim() == 2 and token_table.shape[0] >= R
+    assert token_table.numel() == 0 or token_table.is_contiguous()
+    dev = req_indices.device
+    if out is None:
+        out = {"input_ids": torch.empty(T, dtype=torch.int32, device=dev),
+               "discard_request_mask": torch.empty(R, dtype=torch.uint8, device=dev)}
+        if with_token_indices:
+            out["token_indices"] = torch.empty(T, dtype=torch.int64, device=dev)
+    st = load().pkv_prepare_input_ids(
+        _dev(token_table, torch.int32, "token_table"), int(token_table.shape[1]), R,
+        _dev(req_indices, torch.int32, "req_indices"), _dev(positions, torch.int32, "positions"),
+        T, _dev(seq_lens, torch.int32, "seq_lens"),
+        _dev(num_tokens_total, torch.int32, "num_tokens_total"),
+        _dev(out.get("token_indices"), torch.int64, "token_indices"),
+        _dev(out["input_ids"], torch.int32, "input_ids"),
+        _dev(out["discard_request_mask"], torch.uint8, "discard_request_mask"), _stream(dev))
+    _check(st, "pkv_prepare_input_ids")
+    return out
+
+
+def _pool_block_bytes(key_cache: torch.Tensor, value_cache: torch.Tensor) -> int:
+    assert key_cache.is_contiguous() and value_cache.is_contiguous()
+    assert key_cache.shape[0] == value_cache.shape[0] and key_cache.dtype == value_cache.dtype
+    nb = key_cache.shape[0]
+    per = key_cache.numel() * key_cache.element_size() // max(1, nb)
+    assert per == value_cache.numel() * value_cache.element_size() // max(1, nb)
+    return per
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                block_pairs: torch.Tensor) -> None:
+    """pkv_copy_blocks.  block_pairs: int32 [n, 2] (source, destination) on the
+    pools' device; destinations distinct and never a source."""
+    assert block_pairs.dim() == 2 and block_pairs.shape[1] == 2 and block_pairs.is_contiguous()
+    st = load().pkv_copy_blocks(
+        _dev(key_cache, name="key_cache"), _dev(value_cache, name="value_cache"),
+        key_cache.shape[0], _pool_block_bytes(key_cache, value_cache),
+        _dev(block_pairs, torch.int32, "block_pairs"), int(block_pairs.shape[0]),
+        _stream(key_cache.device))
+    _check(st, "pkv_copy_blocks")
+
+
+def zero_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                block_ids: torch.Tensor) -> None:
+    """pkv_zero_blocks.  block_ids: int32 [n] on the pools' device."""
+    assert block_ids.dim() == 1 and block_ids.is_contiguous()
+    st = load().pkv_zero_blocks(
+        _dev(key_cache, name="key_cache"), _dev(value_cache, name="value_cache"),
+        key_cache.shape[0], _pool_block_bytes(key_cache, value_cache),
+        _dev(block_ids, torch.int32, "block_ids"), int(block_ids.shape[0]),
+        _stream(key_cache.device))
+    _check(st, "pkv_zero_blocks")
 
 
 def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

@@ -10,6 +10,10 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A dispatch counts its work-items in 32 bits: at 256 per workgroup, at most
+// 2^24 - 1 workgroups.
+constexpr int64_t kMaxWorkgroups = (INT64_C(1) << 24) - 1;
+
 pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
 }  // namespace
@@ -48,6 +52,23 @@ pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
       num_scheduled_tokens, num_computed_tokens, block_table, bt_row_stride, num_reqs,
       num_tokens, qsl_len, block_size, num_blocks, req_indices, positions, slot_mapping,
       query_start_loc, seq_lens, logits_indices, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_prepare_input_ids(const int32_t* token_table, int64_t row_width,
+                                 int32_t num_reqs, const int32_t* req_indices,
+                                 const int32_t* positions, int32_t num_tokens,
+                                 const int32_t* seq_lens, const int32_t* num_tokens_total,
+                                 int64_t* token_indices, int32_t* input_ids,
+                                 uint8_t* discard_request_mask, void* stream) {
+  if (num_reqs < 0 || num_tokens < 0 || row_width < 1) return PKV_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (!token_table || !req_indices || !positions || !input_ids))
+    return PKV_ERR_INVALID_ARG;
+  if (num_reqs > 0 && (!seq_lens || !num_tokens_total || !discard_request_mask))
+    return PKV_ERR_INVALID_ARG;
+  return launch_status(pkv::launch_input_ids(
+      token_table, row_width, num_reqs, req_indices, positions, num_tokens, seq_lens,
+      num_tokens_total, token_indices, input_ids, discard_request_mask,
+      static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_kv_cache_write(const void* key, const void* value, int64_t key_row_stride,
@@ -114,6 +135,32 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
                            max_query_len, max_seq_len, split_tokens, dtype, &plan))
     return 0;
   return plan.total_bytes;
+}
+
+pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                           int64_t block_bytes, const int32_t* block_pairs, int32_t num_pairs,
+                           void* stream) {
+  if (num_blocks < 0 || block_bytes < 16 || num_pairs < 0) return PKV_ERR_INVALID_ARG;
+  if (num_pairs > 0 && (!key_cache || !value_cache || !block_pairs)) return PKV_ERR_INVALID_ARG;
+  if ((block_bytes & 15) != 0 || !aligned16(key_cache) || !aligned16(value_cache))
+    return PKV_ERR_UNSUPPORTED;
+  if (pkv::block_op_workgroups(block_bytes, num_pairs) > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_copy_blocks(key_cache, value_cache, num_blocks, block_bytes,
+                                               block_pairs, num_pairs,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_zero_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                           int64_t block_bytes, const int32_t* block_ids, int32_t num_ids,
+                           void* stream) {
+  if (num_blocks < 0 || block_bytes < 16 || num_ids < 0) return PKV_ERR_INVALID_ARG;
+  if (num_ids > 0 && (!key_cache || !value_cache || !block_ids)) return PKV_ERR_INVALID_ARG;
+  if ((block_bytes & 15) != 0 || !aligned16(key_cache) || !aligned16(value_cache))
+    return PKV_ERR_UNSUPPORTED;
+  if (pkv::block_op_workgroups(block_bytes, num_ids) > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;
+  return launch_status(pkv::launch_zero_blocks(key_cache, value_cache, num_blocks, block_bytes,
+                                               block_ids, num_ids,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -40,6 +40,23 @@ hipError_t launch_prepare(const int32_t* nst, const int32_t* nct, const int32_t*
                           int32_t* qsl, int32_t* seq_lens, int32_t* logits_indices,
                           hipStream_t stream);
 
+hipError_t launch_input_ids(const int32_t* token_table, int64_t row_width, int32_t num_reqs,
+                            const int32_t* req_indices, const int32_t* positions,
+                            int32_t num_tokens, const int32_t* seq_lens,
+                            const int32_t* num_tokens_total, int64_t* token_indices,
+                            int32_t* input_ids, uint8_t* discard, hipStream_t stream);
+
+// Workgroups one copy / zero launch takes for `count` blocks (2 pools x chunks).
+int64_t block_op_workgroups(int64_t block_bytes, int32_t count);
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                              int64_t block_bytes, const int32_t* pairs, int32_t num_pairs,
+                              hipStream_t stream);
+
+hipError_t launch_zero_blocks(void* key_cache, void* value_cache, int64_t num_blocks,
+                              int64_t block_bytes, const int32_t* ids, int32_t num_ids,
+                              hipStream_t stream);
+
 hipError_t launch_kv_write(const void* key, const void* value, int64_t key_stride,
                            int64_t value_stride, void* key_cache, void* value_cache,
                            int64_t num_blocks, const int64_t* slot_mapping, int32_t num_tokens,

@@ -136,3 +136,58 @@ hipError_t launch_prepare(const int32_t* nst, const int32_t* nct, const int32_t*
 }
 
 }  // namespace pkv
+
+// ---------------------------------------------------------------------------
+// Input token ids and the discard mask.
+//
+// "Building the Batch" ("How they are computed") keeps every request's token
+// list as one fixed-width row of a 2-D table, so the t-th new token of the
+// request in row r sits at flat offset r * row_width + position; one gather
+// then produces the step's input ids.  "vLLM's Model Runner -- the Persistent
+// Batch, in Source" ("The batch contains rows that must not be sampled")
+// marks a request whose sequence after this pass is still shorter than its
+// known token count: its last row is sampled but the token is thrown away.
+// One thread per flat row and per request; both read what prepare_kernel
+// wrote, so this launch follows it on the same stream.
+// ---------------------------------------------------------------------------
+namespace pkv {
+namespace {
+
+__global__ __launch_bounds__(kThreads) void input_ids_kernel(
+    const int32_t* __restrict__ token_table, int64_t row_width, int32_t num_reqs,
+    const int32_t* __restrict__ req_indices, const int32_t* __restrict__ positions,
+    int32_t num_tokens, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ num_tokens_total, int64_t* __restrict__ token_indices,
+    int32_t* __restrict__ input_ids, uint8_t* __restrict__ discard) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < num_tokens) {
+    const int32_t r = req_indices[i];
+    const int32_t p = positions[i];
+    int64_t k = -1;
+    int32_t id = -1;
+    if (r >= 0 && r < num_reqs && p >= 0 && p < row_width) {
+      k = (int64_t)r * row_width + p;
+      id = token_table[k];
+    }
+    if (token_indices != nullptr) token_indices[i] = k;
+    input_ids[i] = id;
+  }
+  if (i < num_reqs) discard[i] = seq_lens[i] < num_tokens_total[i] ? 1 : 0;
+}
+
+}  // namespace
+
+hipError_t launch_input_ids(const int32_t* token_table, int64_t row_width, int32_t num_reqs,
+                            const int32_t* req_indices, const int32_t* positions,
+                            int32_t num_tokens, const int32_t* seq_lens,
+                            const int32_t* num_tokens_total, int64_t* token_indices,
+                            int32_t* input_ids, uint8_t* discard, hipStream_t stream) {
+  const int32_t n = max(num_tokens, num_reqs);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(input_ids_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, token_table, row_width, num_reqs, req_indices, positions,
+                     num_tokens, seq_lens, num_tokens_total, token_indices, input_ids, discard);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -126,3 +126,45 @@ def test_workspace_sizes():
     # every configuration's workspace is modest next to HBM
     assert ws(17, 2064, 64, 8, 128, 2048, 32768) < (256 << 20)
     assert ws(201, 5200, 32, 8, 128, 5000, 8192) < (256 << 20)
+
+
+def input_ids(lib, **kw):
+    a = dict(tt=FAKE, M=64, R=3, ri=FAKE, pos=FAKE, T=10, sl=FAKE, tot=FAKE, ti=None, ids=FAKE,
+             dm=FAKE)
+    a.update(kw)
+    return lib.pkv_prepare_input_ids(a["tt"], a["M"], a["R"], a["ri"], a["pos"], a["T"],
+                                     a["sl"], a["tot"], a["ti"], a["ids"], a["dm"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(R=-1), dict(T=-1), dict(tt=None),
+                                dict(ri=None), dict(ids=None), dict(sl=None), dict(tot=None),
+                                dict(dm=None)])
+def test_input_ids_rejects(lib, kw):
+    assert input_ids(lib, **kw) == binding.ERR_INVALID_ARG
+
+
+def test_input_ids_empty_is_ok(lib):
+    assert input_ids(lib, T=0, R=0, tt=None, ri=None, pos=None, sl=None, tot=None, ids=None,
+                     dm=None) == binding.OK
+
+
+def block_op(lib, fn, **kw):
+    a = dict(kc=FAKE, vc=FAKE, nb=16, bb=32768, ids=FAKE, n=4)
+    a.update(kw)
+    return getattr(lib, fn)(a["kc"], a["vc"], a["nb"], a["bb"], a["ids"], a["n"], None)
+
+
+@pytest.mark.parametrize("fn", ["pkv_copy_blocks", "pkv_zero_blocks"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(nb=-1), binding.ERR_INVALID_ARG), (dict(bb=8), binding.ERR_INVALID_ARG),
+    (dict(n=-1), binding.ERR_INVALID_ARG), (dict(kc=None), binding.ERR_INVALID_ARG),
+    (dict(ids=None), binding.ERR_INVALID_ARG), (dict(bb=1000), binding.ERR_UNSUPPORTED),
+    (dict(vc=FAKE + 8), binding.ERR_UNSUPPORTED),
+    (dict(bb=1 << 30, n=1 << 20), binding.ERR_UNSUPPORTED)])
+def test_block_ops_reject(lib, fn, kw, code):
+    assert block_op(lib, fn, **kw) == code
+
+
+@pytest.mark.parametrize("fn", ["pkv_copy_blocks", "pkv_zero_blocks"])
+def test_block_ops_empty_is_ok(lib, fn):
+    assert block_op(lib, fn, n=0, kc=None, vc=None, ids=None) == binding.OK
