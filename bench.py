@@ -57,6 +57,14 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="also capture the step in a HIP graph and time K replays; value and "
                         "ms_per_step then come from the replays")
+    p.add_argument("--op", default="step", choices=["step", "input_ids", "copy_blocks",
+                                                     "zero_blocks"],
+                   help="step: the hot path above.  input_ids: prepare_inputs + "
+                        "prepare_input_ids of the workload's step.  copy_blocks / "
+                        "zero_blocks: --blocks block copies (fresh destinations) or clears "
+                        "in both pools of the workload's cache geometry")
+    p.add_argument("--blocks", type=int, default=8192,
+                   help="blocks per copy_blocks / zero_blocks launch")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="instead of the step, time a plain device-to-device copy of this many "
                         "MiB (the known-size kernel that HBM byte counters are scaled by)")
@@ -122,31 +130,34 @@ def algorithmic_work(wl):
     }
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_hbm_traffic.txt")
-TRAFFIC_SOURCES = [os.path.join(ROOT, "paged_kv_cache_prepare_amd", "csrc", f)
-                   for f in ("attention.hip", "pkv_internal.h")]
+_CSRC = os.path.join(ROOT, "paged_kv_cache_prepare_amd", "csrc")
+TRAFFIC = (os.path.join(ROOT, "profiles", "attention_hbm_traffic.txt"),
+           [os.path.join(_CSRC, f) for f in ("attention.hip", "pkv_internal.h")])
+BLOCK_OPS_TRAFFIC = (os.path.join(ROOT, "profiles", "block_ops_hbm_traffic.txt"),
+                     [os.path.join(_CSRC, "block_ops.hip")])
 
 
-def attention_source_hash():
+def source_hash(sources):
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in sources:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(key):
-    """HBM bytes per attention call from the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    figures in profiles/, or None when there are none for this workload or the
-    attention source has changed since they were taken."""
+def measured_traffic(key, which=TRAFFIC):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE figures
+    in profiles/, or None when there are none for this workload or the kernel
+    source has changed since they were taken."""
+    path, sources = which
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             kv = dict(line.split("=", 1) for line in (l.strip() for l in fh)
                       if line and not line.startswith("#") and "=" in line)
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_sha256") != attention_source_hash() or key not in kv:
+    if kv.get("source_sha256") != source_hash(sources) or key not in kv:
         return None
     return int(kv[key])
 
@@ -201,6 +212,154 @@ def cpu_baseline(wl, budget_s):
                       f"on {what} ({dt:.2f} s); fp64"}
 
 
+def _timed_launches(fn, steps, warmup):
+    """Average ms per call of ``fn`` over ``steps`` calls, from HIP events on
+    torch's current stream (the stream the library launches on), after
+    ``warmup`` untimed calls; plus the host-clock ms per call of the same loop."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(steps):
+        fn()
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return ev[0].elapsed_time(ev[1]) / steps, wall
+
+
+def bench_op(args):
+    """One JSON line for a batch-side operation (--op), HBM roofline and the
+    oracle timed beside it."""
+    import torch
+    import oracle
+    import paged_kv_cache_prepare_amd as pkv
+    from paged_kv_cache_prepare_amd import workloads
+
+    dev = torch.device("cuda:0")
+    st = workloads.config_structure(args.workload)
+    nst, nct = st["num_scheduled_tokens"], st["num_computed_tokens"]
+    Hkv, d, bs = st["num_kv_heads"], st["head_dim"], workloads.BLOCK_SIZE
+    rng = np.random.default_rng(2000 + args.workload)
+    line = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded)"}
+    if args.op == "input_ids":
+        R, T = len(nst), int(nst.sum())
+        seq = (nst + nct).astype(np.int64)
+        width = int(seq.max())
+        # requests given more than one token this step are prompt chunks that
+        # do not finish the prompt: their sampled token is discarded
+        total = (seq + (nst > 1)).astype(np.int32)
+        table = rng.integers(0, 152064, (R, width)).astype(np.int32)
+        g = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in
+             dict(nst=nst, nct=nct, total=total, table=table,
+                  bt=np.zeros((R, 1), np.int32)).items()}
+        i32 = dict(dtype=torch.int32, device=dev)
+        prep = {"req_indices": torch.empty(T, **i32), "positions": torch.empty(T, **i32),
+                "slot_mapping": torch.empty(T, dtype=torch.int64, device=dev),
+                "query_start_loc": torch.empty(R + 1, **i32), "seq_lens": torch.empty(R, **i32),
+                "logits_indices": torch.empty(R, **i32)}
+        ids = {"input_ids": torch.empty(T, **i32),
+               "discard_request_mask": torch.empty(R, dtype=torch.uint8, device=dev)}
+
+        def fn():
+            pkv.prepare_inputs(g["nst"], g["nct"], g["bt"], num_tokens=T, block_size=1 << 30,
+                               num_blocks=1, out=prep)
+            pkv.prepare_input_ids(g["table"], prep["req_indices"], prep["positions"],
+                                  prep["seq_lens"], g["total"], out=ids)
+
+        ms, wall = _timed_launches(fn, args.steps, args.warmup)
+        # prepare: nst, nct, table column read, 3 per-row + 3 per-request outputs;
+        # ids: req_indices, positions, token id read + write; seq_lens, total, mask
+        nbytes = R * 8 + T * 4 + T * 16 + R * 12 + T * 16 + R * 9
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) or reps == 0:
+            ref = oracle.prepare(nst, nct, np.zeros((R, 1), np.int32), 1 << 30, 1)
+            oracle.input_ids(table, ref["req_indices"], ref["positions"], ref["seq_lens"], total)
+            reps += 1
+        cpu_s = (time.perf_counter() - t0) / reps
+        gbs = nbytes / (ms / 1e3) / 1e9
+        line.update({
+            "metric": "input prep tokens/s (prepare_inputs + prepare_input_ids)",
+            "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "dtype": "int32",
+            "config": {"workload": workloads.CONFIG_NAMES[args.workload], "op": args.op,
+                       "num_reqs": R, "num_tokens": T, "row_width": width},
+            "host_ms_per_step": round(wall, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None,
+                         "kernel": "prepare_kernel + input_ids_kernel (launch-latency bound)",
+                         "algorithmic_bytes": nbytes, "avg_ms": round(ms, 4)},
+            "cpu_baseline": {"value": round(T / cpu_s, 1), "unit": "tokens/s", "cores": 1,
+                             "kind": "oracle",
+                             "sample": f"oracle prepare + input_ids on the whole step, "
+                                       f"{reps} times"}})
+        print(json.dumps(line), flush=True)
+        return
+
+    # copy_blocks / zero_blocks on the workload's pool geometry
+    fp8 = args.kv_dtype == "fp8"
+    e = 1 if fp8 else (4 if st["dtype"] == torch.float32 else 2)
+    block_bytes = Hkv * bs * d * e
+    need = int(((nst.astype(np.int64) + nct + bs - 1) // bs).sum())
+    nb = max(int(math.ceil(1.25 * need)), 2 * args.blocks)
+    n = args.blocks
+    gen = torch.Generator(device=dev).manual_seed(2000 + args.workload)
+    pools = [torch.randint(0, 256, (nb, block_bytes), generator=gen, dtype=torch.uint8,
+                           device=dev) for _ in range(2)]
+    perm = rng.permutation(nb)
+    if args.op == "copy_blocks":
+        items = np.stack([rng.choice(perm[n:], n), perm[:n]], 1).astype(np.int32)
+        moved = 2 * 2 * n * block_bytes                 # both pools, read + write
+    else:
+        items = perm[:n].astype(np.int32)
+        moved = 2 * n * block_bytes                     # both pools, write
+    dev_items = torch.from_numpy(np.ascontiguousarray(items)).to(dev)
+    op = getattr(pkv, args.op)
+    ms, wall = _timed_launches(lambda: op(pools[0], pools[1], dev_items), args.steps,
+                               args.warmup)
+    gbs = moved / (ms / 1e3) / 1e9
+    # oracle on host pools: a bounded sample of the same list in a compact pool
+    m = min(n, 1024)
+    hk = np.zeros((2 * m, block_bytes), np.uint8)
+    hv = np.zeros((2 * m, block_bytes), np.uint8)
+    h_items = (np.stack([np.arange(m, 2 * m), np.arange(m)], 1) if args.op == "copy_blocks"
+               else np.arange(m)).astype(np.int32)
+    ofn = oracle.copy_blocks if args.op == "copy_blocks" else oracle.zero_blocks
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) or reps == 0:
+        ofn(hk, hv, h_items)
+        reps += 1
+    cpu_s = (time.perf_counter() - t0) / reps
+    line.update({
+        "metric": f"{args.op} HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+        "ms_per_step": round(ms, 4), "dtype": "u8",
+        "config": {"workload": f"{n} blocks of {block_bytes} B per pool, pools of "
+                               f"{workloads.CONFIG_NAMES[args.workload]}"
+                               + (" with an FP8 cache" if fp8 else ""),
+                   "op": args.op, "blocks": n, "block_bytes": block_bytes,
+                   "num_blocks": nb},
+        "host_ms_per_step": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"{args.op}_w{args.workload}_n{n}"
+                                                 + ("_fp8" if fp8 else ""), BLOCK_OPS_TRAFFIC),
+                     "kernel": f"{args.op}_kernel, HIP events", "algorithmic_bytes": moved,
+                     "avg_ms": round(ms, 4)},
+        "cpu_baseline": {"value": round((moved * m / n) / cpu_s / 1e9, 2), "unit": "GB/s",
+                         "cores": 1, "kind": "oracle",
+                         "sample": f"oracle {args.op} of {m} blocks in a {2 * m}-block host "
+                                   f"pool pair, {reps} times"}})
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -209,6 +368,9 @@ def main():
         sys.exit(2)
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.op != "step":
+        bench_op(args)
         return
     import torch
     import paged_kv_cache_prepare_amd as pkv

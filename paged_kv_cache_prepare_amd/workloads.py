@@ -321,5 +321,9 @@ def config_structure(idx: int, seed: int | None = None) -> dict:
         nct = np.concatenate([np.full(16, 32767), [0]])
     else:
         raise ValueError(idx)
+    heads = {1: (4, 2, 64), 2: (40, 40, 128), 3: (32, 8, 128), 4: (32, 8, 128),
+             5: (64, 8, 128)}[idx]
     return {"num_scheduled_tokens": nst.astype(np.int32),
-            "num_computed_tokens": nct.astype(np.int32)}
+            "num_computed_tokens": nct.astype(np.int32),
+            "num_q_heads": heads[0], "num_kv_heads": heads[1], "head_dim": heads[2],
+            "dtype": torch.float32 if idx == 1 else torch.bfloat16}

@@ -56,3 +56,15 @@ def test_select_keeps_rows_of_chosen_requests():
     assert np.array_equal(sub.block_table, wl.block_table[[2, 0]])
     assert torch.equal(sub.q, torch.cat([wl.q[4:6], wl.q[0:3]]))
     assert sub.key_cache is wl.key_cache
+
+
+def test_config_structure_geometry_matches_the_configs():
+    wl = workloads.config(1)
+    s = workloads.config_structure(1)
+    assert (s["num_q_heads"], s["num_kv_heads"], s["head_dim"], s["dtype"]) == \
+        (wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.dtype)
+    for idx in (2, 3, 4, 5):
+        s = workloads.config_structure(idx)
+        name = workloads.CONFIG_NAMES[idx]
+        assert f"Hq {s['num_q_heads']} / Hkv {s['num_kv_heads']}, d {s['head_dim']}" in name
+        assert s["dtype"] == torch.bfloat16 and "bf16" in name
