@@ -251,3 +251,47 @@ def test_attention_prefix_that_diverges_and_rejoins():
     for st in (32, 64, 128):
         _, _, _, out = gpu_step(wl, split_tokens=st)
         assert_attention_close(out, ref, wl.dtype, f"diverging prefix, split {st}")
+
+
+def _shape_scores(wl, growth, seed):
+    """Give every key of kv head h the direction u_h scaled by growth[r](pos),
+    plus noise, and every query of that head's group u_h plus noise, so that a
+    row's scores follow growth[r] along the key axis.  Steep growth makes the
+    running maximum jump by far more than the kernels' lazy-rescale bound
+    within one step of keys, so every rescale path runs."""
+    g = torch.Generator().manual_seed(seed)
+    H, d, G = wl.num_kv_heads, wl.head_dim, wl.num_q_heads // wl.num_kv_heads
+    u = torch.where(torch.rand(H, d, generator=g) < 0.5, -1.0, 1.0)
+    kc = wl.key_cache.float().cpu()
+    for r, f in enumerate(growth):
+        for p in range(int(wl.num_computed_tokens[r])):
+            b, off = int(wl.block_table[r, p // 16]), p % 16
+            kc[b, :, off, :] = f(p) * u + 0.5 * torch.randn(H, d, generator=g)
+    key = wl.key.float().cpu()
+    qsl = np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)])
+    for r, f in enumerate(growth):
+        for t in range(int(wl.num_scheduled_tokens[r])):
+            key[qsl[r] + t] = f(int(wl.num_computed_tokens[r]) + t) * u + \
+                0.5 * torch.randn(H, d, generator=g)
+    q = u.repeat_interleave(G, 0)[None] + 0.5 * torch.randn(wl.num_tokens, H * G, d, generator=g)
+    dev = wl.key_cache.device
+    wl.key_cache = kc.to(wl.dtype).to(dev)
+    wl.key = key.to(wl.dtype).to(dev)
+    wl.q = q.to(wl.dtype).to(dev)
+    return wl
+
+
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_attention_scores_that_keep_growing(split_tokens):
+    """Scores that grow by about 20 log2 units every 32 keys (twice the lazy
+    rescale bound per half step of a prompt tile), fall, or spike at sparse
+    positions: prompt chunks and decodes against the fp64 oracle."""
+    wl = workloads.build("grow", [150, 1, 100, 1, 70], [200, 700, 0, 900, 330], num_q_heads=16,
+                         num_kv_heads=4, head_dim=128, seed=61, device=device(), pool_slack=1.2)
+    growth = [lambda p: 0.04 * p, lambda p: 0.04 * p, lambda p: 3.0 if p % 37 == 5 else -0.2,
+              lambda p: 30.0 - 0.03 * p, lambda p: 0.02 * p * (1 if (p // 40) % 2 else -1)]
+    wl = _shape_scores(wl, growth, 62)
+    _, _, _, out = gpu_step(wl, split_tokens=split_tokens)
+    _, _, _, ref = oracle_step(wl)
+    assert torch.isfinite(out).all()
+    assert_attention_close(out, ref, wl.dtype, f"growing scores split {split_tokens}")
