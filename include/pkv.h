@@ -307,8 +307,11 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
  * rounded to nearest even.
  * Errors: PKV_ERR_INVALID_ARG (null pointers, sizes, num_q_heads not a
  * multiple of num_kv_heads, row strides too small, split_tokens not a
- * multiple of 32, scale not finite and positive); PKV_ERR_UNSUPPORTED (head_dim not 64/128, block_size not
- * 16, more than 16 q heads per kv head); PKV_ERR_WORKSPACE; PKV_ERR_LAUNCH.
+ * multiple of 32, scale not finite and positive); PKV_ERR_UNSUPPORTED
+ * (head_dim not 64/128, block_size not 16, more than 16 q heads per kv head,
+ * or a work list longer than 2^24 - 1 items: one item per (request, kv head,
+ * context partition) plus the prompt tiles -- only reachable with tiny forced
+ * partitions of very long contexts); PKV_ERR_WORKSPACE; PKV_ERR_LAUNCH.
  */
 pkv_status pkv_paged_attention_varlen(
     const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,

@@ -182,6 +182,7 @@ __device__ inline int first_not_above(const int* s, int n, int x) {
 struct PlanSmem {
   int wave[16];
   int len[kPlanReqs];    // seq_len by request (ordered path)
+  int qlen[kPlanReqs];   // valid query rows by request (ordered path)
   int req[kPlanReqs];    // request at rank j (ordered path) / unused (chunked path)
   int incl[kPlanReqs];   // inclusive prefix of per-slot unit counts
   int aux[kPlanReqs];    // per-slot split count or tile count
@@ -191,7 +192,19 @@ struct PlanSmem {
 };
 
 // Work units of one request in a pass: prefill tiles (pass 0) or decode
-// partitions (pass 1).  *aux gets the tile count or the split count.
+// partitions (pass 1), from its valid query rows and seq_len.  *aux gets the
+// tile count or the split count.
+__device__ inline int plan_units_of(int q_len, int seq_len, int group, int split_tokens,
+                                    int max_splits, int pass, int* aux) {
+  const int pairs = q_len * group;
+  int cnt = 0;
+  if (pass == 0 && pairs > kPairsPerTile) cnt = ceil_div(pairs, kPrefillPairs);
+  if (pass == 1 && pairs >= 1 && pairs <= kPairsPerTile)
+    cnt = num_splits(seq_len, split_tokens, max_splits);
+  *aux = cnt;
+  return cnt;
+}
+
 __device__ inline int plan_units(const int32_t* qsl, const int32_t* seq_lens, int r,
                                  int num_tokens, int group, int split_tokens, int max_splits,
                                  int pass, int* aux) {
@@ -228,8 +241,13 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
   const bool ordered = num_reqs <= kPlanReqs && max_splits <= kPlanMaxSplits;
 
   if (ordered) {
+    // every per-request input is read once, up front, in one round trip
     const int L = tid < num_reqs ? seq_lens[tid] : 0;
-    if (tid < num_reqs) sm.len[tid] = L;
+    const int QL = tid < num_reqs ? valid_q_len(qsl, tid, num_tokens) : 0;
+    if (tid < num_reqs) {
+      sm.len[tid] = L;
+      sm.qlen[tid] = QL;
+    }
     __syncthreads();
     if (tid < num_reqs) {
       int rank = 0;
@@ -243,18 +261,18 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     // pass 0: prefill tiles, in rank order
     {
       int tiles = 0;
-      if (tid < num_reqs)
-        plan_units(qsl, seq_lens, sm.req[tid], num_tokens, group, split_tokens, max_splits, 0,
-                   &tiles);
+      if (tid < num_reqs) {
+        const int rq = sm.req[tid];
+        plan_units_of(sm.qlen[rq], sm.len[rq], group, split_tokens, max_splits, 0, &tiles);
+      }
       int total;
       const int incl = block_scan_1024(tiles, sm.wave, &total);
       sm.incl[tid] = incl;
       sm.aux[tid] = tiles;
       __syncthreads();
-      const int64_t n = (int64_t)total * H;
-      for (int64_t e = tid; e < n; e += kPlanReqs) {
-        if (e >= max_items) break;
-        const int u = (int)(e / H), h = (int)(e - (int64_t)u * H);
+      const int n = (int)min((int64_t)total * H, max_items);
+      for (int e = tid; e < n; e += kPlanReqs) {
+        const int u = e / H, h = e - u * H;
         const int j = upper_bound_lds(sm.incl, num_reqs, u);
         const int k = u - (sm.incl[j] - sm.aux[j]);
         items[e] = make_int4(sm.req[j], h, sm.aux[j] - 1 - k, -1);
@@ -264,8 +282,10 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     // pass 1: decode partitions, partition-major over the decode requests in rank order
     {
       int ns = 0;
-      if (tid < num_reqs)
-        plan_units(qsl, seq_lens, sm.req[tid], num_tokens, group, split_tokens, max_splits, 1, &ns);
+      if (tid < num_reqs) {
+        const int rq = sm.req[tid];
+        plan_units_of(sm.qlen[rq], sm.len[rq], group, split_tokens, max_splits, 1, &ns);
+      }
       int nd;
       const int ci = block_scan_1024(ns > 0 ? 1 : 0, sm.wave, &nd) - 1;
       if (ns > 0) {
@@ -285,12 +305,11 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
       }
       if (tid == 0) sm.pk[0] = 0;
       __syncthreads();
-      const int64_t base = carry * H;
-      const int64_t n = (int64_t)pcarry * H;
-      for (int64_t e = tid; e < n; e += kPlanReqs) {
-        const int64_t idx = base + e;
-        if (idx >= max_items) break;
-        const int u = (int)(e / H), h = (int)(e - (int64_t)u * H);
+      const int base = (int)min(carry * H, max_items);
+      const int n = (int)min((int64_t)pcarry * H, max_items - base);
+      for (int e = tid; e < n; e += kPlanReqs) {
+        const int idx = base + e;
+        const int u = e / H, h = e - u * H;
         const int k = upper_bound_lds(sm.pk, max_splits + 1, u) - 1;
         const int j = u - sm.pk[k];
         items[idx] = make_int4(sm.dreq[j], h, k, sm.dns[j]);

@@ -168,3 +168,8 @@ def test_block_ops_reject(lib, fn, kw, code):
 @pytest.mark.parametrize("fn", ["pkv_copy_blocks", "pkv_zero_blocks"])
 def test_block_ops_empty_is_ok(lib, fn):
     assert block_op(lib, fn, n=0, kc=None, vc=None, ids=None) == binding.OK
+
+
+def test_attention_rejects_a_work_list_past_the_dispatch_limit(lib):
+    # 32-token partitions of 2^30-token contexts: far more than 2^24 - 1 items
+    assert attn(lib, R=1000, T=1000, mq=1, ms=1 << 30, split=32) == binding.ERR_UNSUPPORTED
