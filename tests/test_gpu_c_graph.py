@@ -99,3 +99,92 @@ def test_step_replays_in_a_hip_graph():
         log(f"  replay {rep}: bit-identical to the eager step")
         # eager work between replays on the same stream
         eager_reference()
+
+
+def test_input_prep_and_block_ops_replay_in_a_hip_graph():
+    """The batch-side calls are capturable too: prepare -> input-id gather ->
+    a block copy-on-write and a clear of fresh blocks -> KV write ->
+    attention, captured once and replayed, every replay bit-identical to the
+    eager sequence (the clear is a kernel, not a memset node)."""
+    dev = device()
+    wl = workloads.build("graph2", [1, 1, 30, 1], [500, 47, 64, 1300], num_q_heads=8,
+                         num_kv_heads=2, head_dim=128, seed=29, device=dev, pool_slack=1.5)
+    nb = wl.num_blocks
+    used = set(wl.block_table[wl.block_table >= 0].tolist())
+    spare = [b for b in range(nb) if b not in used]
+    assert len(spare) >= 4
+    nst = torch.from_numpy(wl.num_scheduled_tokens).to(dev)
+    nct = torch.from_numpy(wl.num_computed_tokens).to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    M = int(wl.max_seq_len) + 8
+    g = torch.Generator(device=dev).manual_seed(3)
+    table = torch.randint(0, 50000, (wl.num_reqs, M), generator=g, device=dev, dtype=torch.int32)
+    total = torch.tensor((wl.num_scheduled_tokens + wl.num_computed_tokens + [0, 5, 0, 1])
+                         .astype("int32"), device=dev)
+    # copy a used block to a spare one, clear two other spare blocks
+    pairs = torch.tensor([[int(wl.block_table[0, 0]), spare[0]]], dtype=torch.int32, device=dev)
+    clear = torch.tensor(spare[1:3], dtype=torch.int32, device=dev)
+    kc0, vc0 = wl.key_cache.clone(), wl.value_cache.clone()
+    kc, vc = kc0.clone(), vc0.clone()
+    out = torch.empty_like(wl.q)
+    prep, ws = _buffers(wl, dev)
+    ids = {"input_ids": torch.empty(wl.num_tokens, dtype=torch.int32, device=dev),
+           "discard_request_mask": torch.empty(wl.num_reqs, dtype=torch.uint8, device=dev),
+           "token_indices": torch.empty(wl.num_tokens, dtype=torch.int64, device=dev)}
+
+    def step():
+        pkv.prepare_inputs(nst, nct, bt, num_tokens=wl.num_tokens, block_size=wl.block_size,
+                           num_blocks=nb, out=prep)
+        pkv.prepare_input_ids(table, prep["req_indices"], prep["positions"], prep["seq_lens"],
+                              total, out=ids)
+        pkv.copy_blocks(kc, vc, pairs)
+        pkv.zero_blocks(kc, vc, clear)
+        pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"],
+                           block_size=wl.block_size)
+        pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                            scale=wl.scale, out=out, split_tokens=64, workspace=ws)
+
+    def eager_reference():
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        step()
+        torch.cuda.synchronize()
+        return ({k: v.clone() for k, v in {**prep, **ids}.items()}, kc.clone(), vc.clone(),
+                out.clone())
+
+    ref = eager_reference()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    kc.copy_(kc0)
+    vc.copy_(vc0)
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        out.fill_(float("nan"))
+        for v in list(prep.values()) + list(ids.values()):
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        rp, rk, rv, ro = ref
+        for k in rp:
+            cur = prep[k] if k in prep else ids[k]
+            assert torch.equal(cur, rp[k]), f"replay {rep}: {k}"
+        assert torch.equal(bits_view(kc), bits_view(rk)), f"replay {rep}: K pool"
+        assert torch.equal(bits_view(vc), bits_view(rv)), f"replay {rep}: V pool"
+        assert torch.equal(bits_view(out), bits_view(ro)), f"replay {rep}: attention output"
+        assert not bits_view(kc[spare[1]]).any() and not bits_view(vc[spare[2]]).any()
+        assert torch.equal(bits_view(kc[spare[0]]), bits_view(kc0[int(wl.block_table[0, 0])]))
+        log(f"  replay {rep}: bit-identical to the eager sequence")
+        eager_reference()
