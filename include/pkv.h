@@ -2,8 +2,8 @@
  * pkv.h -- C ABI of libpkv: paged KV-cache input preparation, KV-cache write
  * and paged variable-length causal attention for AMD Instinct MI355X (gfx950).
  *
- * One step of paged LLM serving runs three calls, in this order, on one HIP
- * stream:
+ * One step of paged LLM serving runs these calls on one HIP stream (the
+ * index derivation first, the KV write before the attention that reads it):
  *
  *   pkv_prepare_inputs         flat-batch index tensors from the scheduler's
  *                              per-request token counts and block tables;
@@ -24,6 +24,10 @@
  *   pkv_zero_blocks            whole-block clears in both pools (freshly
  *                              allocated blocks).
  *
+ * Two more calls describe the build: pkv_debug_checks_enabled and
+ * pkv_debug_check_flags (the checked build, libpkv_checked.so, validates
+ * every call's device data first; see PKV_ERR_DEVICE_DATA below).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers named as device pointers must be device memory (or memory the
@@ -31,6 +35,8 @@
  *   keeps no device state between calls, never synchronises, never reads
  *   device memory from the host, and only enqueues work on `stream`
  *   (a hipStream_t; NULL means the default stream).  Calls are reentrant.
+ *   (The checked build is the exception: it reads a check word back and
+ *   synchronises `stream` once per call.)
  * - Host-side validation covers the scalar arguments and null pointers only;
  *   it returns a status and enqueues nothing on failure.  Device-side
  *   contents are preconditions (listed per call).  Where a precondition on
@@ -65,8 +71,35 @@ typedef enum pkv_status {
   PKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes  */
   PKV_ERR_UNSUPPORTED = 2, /* a valid argument this build has no kernel for    */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
-  PKV_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch         */
+  PKV_ERR_LAUNCH = 4,      /* the HIP runtime rejected a kernel launch         */
+  PKV_ERR_DEVICE_DATA = 5  /* checked build only: device data broke a
+                              precondition (see pkv_debug_check_flags)        */
 } pkv_status;
+
+/*
+ * The checked build (libpkv_checked.so, compiled with PKV_DEBUG_CHECKS)
+ * exports the same entry points.  Each first runs a validation kernel on the
+ * device data it is given, on `stream`, waits for it (the checked build does
+ * synchronise), and returns PKV_ERR_DEVICE_DATA without launching anything
+ * else when a precondition is broken; pkv_debug_check_flags() then returns
+ * the failed checks as these bits.  The regular build never checks device
+ * data and never returns PKV_ERR_DEVICE_DATA.
+ */
+#define PKV_CHECK_COUNTS 0x001u    /* negative token counts, or their sum != num_tokens */
+#define PKV_CHECK_BLOCK_ID 0x002u  /* a table entry the call reads is outside
+                                      [0, num_blocks), or its column is past the row   */
+#define PKV_CHECK_SLOT 0x004u      /* a slot outside [-1, num_blocks * block_size)     */
+#define PKV_CHECK_SLOT_DUP 0x008u  /* two rows of one write share a slot (checked up
+                                      to 65536 rows)                                   */
+#define PKV_CHECK_QSL 0x010u       /* query_start_loc negative, decreasing, or past
+                                      num_tokens                                       */
+#define PKV_CHECK_LENGTHS 0x020u   /* q_len > seq_len, seq_len > max_seq_len or
+                                      q_len > max_query_len                            */
+#define PKV_CHECK_ROW 0x040u       /* input ids: a row's request or position outside
+                                      the token table (other than a -1, -1 padding row) */
+#define PKV_CHECK_PAIRS 0x080u     /* block copies: a destination repeated or also a
+                                      source (checked up to 65536 pairs)               */
+#define PKV_CHECK_SCALE 0x100u     /* an FP8 scale not finite and positive             */
 
 typedef enum pkv_dtype {
   PKV_F32 = 0,  /* IEEE binary32                                   */
@@ -75,6 +108,14 @@ typedef enum pkv_dtype {
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* pkv_status_string(pkv_status status);
+
+/* 1 in the checked build, 0 in the regular one. */
+int32_t pkv_debug_checks_enabled(void);
+
+/* Checked build: the PKV_CHECK_* bits of the last call that returned
+ * PKV_ERR_DEVICE_DATA in this process (0 before any; not per thread).
+ * Regular build: always 0. */
+uint32_t pkv_debug_check_flags(void);
 
 /*
  * pkv_prepare_inputs -- flat-batch index tensors for one step.

@@ -1,9 +1,11 @@
-"""Build libpkv.so (HIP, gfx950) in-tree with hipcc.
+"""Build libpkv.so and libpkv_checked.so (HIP, gfx950) in-tree with hipcc.
 
-Every source under csrc/ is compiled to an object in parallel, then linked
-into ``paged_kv_cache_prepare_amd/libpkv.so``.  Packed-fp32 instructions are
-switched off for all device code (``-packed-fp32-ops``).  ``FILE_FLAGS`` adds
-per-file options.
+Every source under csrc/ is compiled to an object in parallel and linked
+into ``paged_kv_cache_prepare_amd/libpkv.so``.  The checked build
+(``libpkv_checked.so``) links the same kernels with api.hip compiled again
+under ``PKV_DEBUG_CHECKS`` and the validation kernels of checks.hip.
+Packed-fp32 instructions are switched off for all device code
+(``-packed-fp32-ops``).  ``FILE_FLAGS`` adds per-file options.
 """
 from __future__ import annotations
 
@@ -18,7 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
-SOURCES = ["api.hip", "prepare.hip", "kv_write.hip", "block_ops.hip", "attention.hip"]
+CHECKED_LIB_PATH = os.path.join(HERE, "libpkv_checked.so")
+KERNEL_SOURCES = ["prepare.hip", "kv_write.hip", "block_ops.hip", "attention.hip"]
+SOURCES = ["api.hip", *KERNEL_SOURCES]
 # Per-file flags.  The attention kernels never feed a NaN into a max or a sum
 # (masked scores are selected away first), so max operations need no NaN
 # canonicalisation.
@@ -40,13 +44,15 @@ def compile_flags(extra=()) -> list[str]:
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile and link libpkv.so.  Always rebuilds.  Returns the library path."""
+    """Compile and link libpkv.so and libpkv_checked.so.  Always rebuilds.
+    Returns the path of libpkv.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
 
-    def one(src):
-        obj = os.path.join(BUILD_DIR, src.rsplit(".", 1)[0] + ".o")
-        cmd = [cc, *compile_flags([*FILE_FLAGS.get(src, []), *extra_flags]), "-c",
+    def one(job):
+        src, name, flags = job
+        obj = os.path.join(BUILD_DIR, name)
+        cmd = [cc, *compile_flags([*FILE_FLAGS.get(src, []), *flags, *extra_flags]), "-c",
                os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
@@ -55,14 +61,19 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             print(r.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    jobs = [(src, src.rsplit(".", 1)[0] + ".o", []) for src in SOURCES]
+    jobs += [("api.hip", "api_checked.o", ["-DPKV_DEBUG_CHECKS"]), ("checks.hip", "checks.o", [])]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip((j[1] for j in jobs), ex.map(one, jobs)))
+    kernels = [objs[src.rsplit(".", 1)[0] + ".o"] for src in KERNEL_SOURCES]
+    for path, own in ((LIB_PATH, [objs["api.o"]]),
+                      (CHECKED_LIB_PATH, [objs["api_checked.o"], objs["checks.o"]])):
+        tmp = path + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *own, *kernels, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -4,6 +4,10 @@ Argument marshalling only: tensors are passed as device pointers, sizes as
 host integers, and the current torch stream as the HIP stream.  Every step of
 the computation runs in the library's HIP kernels; there is no Python or CPU
 fallback.  If the library is not built this module raises.
+
+With the environment variable PKV_DEBUG_CHECKS=1 (or after ``use_checked()``)
+the checked build libpkv_checked.so is loaded instead: same entry points, plus
+device-side validation of every call's device data (it synchronises).
 """
 from __future__ import annotations
 
@@ -13,11 +17,18 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+HERE = os.path.dirname(os.path.abspath(__file__))
+REGULAR_LIB_PATH = os.path.join(HERE, "libpkv.so")
+CHECKED_LIB_PATH = os.path.join(HERE, "libpkv_checked.so")
+LIB_PATH = CHECKED_LIB_PATH if os.environ.get("PKV_DEBUG_CHECKS") == "1" else REGULAR_LIB_PATH
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE_DATA = range(6)
+# PKV_CHECK_* bits of the checked build (include/pkv.h)
+CHECK_BITS = {"counts": 0x001, "block_id": 0x002, "slot": 0x004, "slot_dup": 0x008, "qsl": 0x010,
+              "lengths": 0x020, "row": 0x040, "pairs": 0x080, "scale": 0x100}
 F32, BF16 = 0, 1
-EXPORTS = ("pkv_status_string", "pkv_prepare_inputs", "pkv_prepare_input_ids",
+EXPORTS = ("pkv_status_string", "pkv_debug_checks_enabled", "pkv_debug_check_flags",
+           "pkv_prepare_inputs", "pkv_prepare_input_ids",
            "pkv_kv_cache_write", "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
            "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8", "pkv_copy_blocks",
            "pkv_zero_blocks")
@@ -44,6 +55,10 @@ def load() -> ctypes.CDLL:
                             ctypes.c_size_t)
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_debug_checks_enabled.argtypes = []
+    lib.pkv_debug_checks_enabled.restype = ctypes.c_int32
+    lib.pkv_debug_check_flags.argtypes = []
+    lib.pkv_debug_check_flags.restype = ctypes.c_uint32
     lib.pkv_prepare_inputs.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P, P, P, P, P]
     lib.pkv_prepare_inputs.restype = ctypes.c_int
     lib.pkv_prepare_input_ids.argtypes = [P, i64, i32, P, P, i32, P, P, P, P, P, P]
@@ -73,6 +88,20 @@ def load() -> ctypes.CDLL:
     return lib
 
 
+def use_checked(checked: bool = True) -> ctypes.CDLL:
+    """Switch this process to the checked (or back to the regular) build."""
+    global _lib, LIB_PATH
+    LIB_PATH = CHECKED_LIB_PATH if checked else REGULAR_LIB_PATH
+    _lib = None
+    return load()
+
+
+def check_flags() -> list[str]:
+    """Names of the checks the last PKV_ERR_DEVICE_DATA call failed (checked build)."""
+    bits = int(load().pkv_debug_check_flags())
+    return [name for name, bit in CHECK_BITS.items() if bits & bit]
+
+
 def status_string(status: int) -> str:
     return load().pkv_status_string(int(status)).decode()
 
@@ -100,6 +129,8 @@ def _stream(device: torch.device) -> int:
 
 
 def _check(status: int, what: str):
+    if status == ERR_DEVICE_DATA:
+        raise PkvError(status, f"{what} (failed checks: {', '.join(check_flags())})")
     if status != OK:
         raise PkvError(status, what)
 

@@ -14,6 +14,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // 2^24 - 1 workgroups.
 constexpr int64_t kMaxWorkgroups = (INT64_C(1) << 24) - 1;
 
+// The checked build validates device data before launching (checks.hip); the
+// regular build compiles the checks away without evaluating them.
+#ifdef PKV_DEBUG_CHECKS
+#define PKV_CHECK(call)                  \
+  do {                                   \
+    const pkv_status check_ = (call);    \
+    if (check_ != PKV_OK) return check_; \
+  } while (0)
+#else
+#define PKV_CHECK(call) \
+  do {                  \
+  } while (0)
+#endif
+
 pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
 }  // namespace
@@ -27,8 +41,25 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_DEVICE_DATA: return "device data breaks a precondition (checked build)";
   }
   return "unknown status";
+}
+
+int32_t pkv_debug_checks_enabled(void) {
+#ifdef PKV_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+uint32_t pkv_debug_check_flags(void) {
+#ifdef PKV_DEBUG_CHECKS
+  return pkv::last_check_flags();
+#else
+  return 0u;
+#endif
 }
 
 pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
@@ -48,6 +79,9 @@ pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
   if (num_tokens > 0 && (num_reqs == 0 || !block_table || bt_row_stride < 1 || !req_indices ||
                          !positions || !slot_mapping))
     return PKV_ERR_INVALID_ARG;
+  PKV_CHECK(pkv::check_prepare(num_scheduled_tokens, num_computed_tokens, block_table,
+                               bt_row_stride, num_reqs, num_tokens, block_size, num_blocks,
+                               static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_prepare(
       num_scheduled_tokens, num_computed_tokens, block_table, bt_row_stride, num_reqs,
       num_tokens, qsl_len, block_size, num_blocks, req_indices, positions, slot_mapping,
@@ -65,6 +99,8 @@ pkv_status pkv_prepare_input_ids(const int32_t* token_table, int64_t row_width,
     return PKV_ERR_INVALID_ARG;
   if (num_reqs > 0 && (!seq_lens || !num_tokens_total || !discard_request_mask))
     return PKV_ERR_INVALID_ARG;
+  PKV_CHECK(pkv::check_rows(req_indices, positions, num_tokens, num_reqs, row_width,
+                            static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_input_ids(
       token_table, row_width, num_reqs, req_indices, positions, num_tokens, seq_lens,
       num_tokens_total, token_indices, input_ids, discard_request_mask,
@@ -89,6 +125,8 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, int64_t key_ro
       key_row_stride * esz % 16 != 0 || value_row_stride * esz % 16 != 0)
     return PKV_ERR_INVALID_ARG;
   if (num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  PKV_CHECK(pkv::check_slots(slot_mapping, num_tokens, num_blocks * block_size, nullptr,
+                             nullptr, static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_kv_write(key, value, key_row_stride, value_row_stride,
                                             key_cache, value_cache, num_blocks, slot_mapping,
                                             num_tokens, num_kv_heads, head_dim, block_size, esz,
@@ -119,6 +157,8 @@ pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, int64_t ke
       (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0)
     return PKV_ERR_INVALID_ARG;
   if (num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  PKV_CHECK(pkv::check_slots(slot_mapping, num_tokens, num_blocks * pkv::kBlock, k_scale,
+                             v_scale, static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_kv_write_fp8(key, value, key_row_stride, value_row_stride,
                                                 key_cache, value_cache, num_blocks, slot_mapping,
                                                 num_tokens, num_kv_heads, head_dim, esz, k_scale,
@@ -145,6 +185,8 @@ pkv_status pkv_copy_blocks(void* key_cache, void* value_cache, int64_t num_block
   if ((block_bytes & 15) != 0 || !aligned16(key_cache) || !aligned16(value_cache))
     return PKV_ERR_UNSUPPORTED;
   if (pkv::block_op_workgroups(block_bytes, num_pairs) > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;
+  PKV_CHECK(pkv::check_block_list(block_pairs, num_pairs, true, num_blocks,
+                                  static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_copy_blocks(key_cache, value_cache, num_blocks, block_bytes,
                                                block_pairs, num_pairs,
                                                static_cast<hipStream_t>(stream)));
@@ -158,6 +200,8 @@ pkv_status pkv_zero_blocks(void* key_cache, void* value_cache, int64_t num_block
   if ((block_bytes & 15) != 0 || !aligned16(key_cache) || !aligned16(value_cache))
     return PKV_ERR_UNSUPPORTED;
   if (pkv::block_op_workgroups(block_bytes, num_ids) > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;
+  PKV_CHECK(pkv::check_block_list(block_ids, num_ids, false, num_blocks,
+                                  static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_zero_blocks(key_cache, value_cache, num_blocks, block_bytes,
                                                block_ids, num_ids,
                                                static_cast<hipStream_t>(stream)));
@@ -229,6 +273,9 @@ static pkv_status attention_call(
   a.k_scale = kv8 ? k_scale : nullptr;
   a.v_scale = kv8 ? v_scale : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  PKV_CHECK(pkv::check_attention(query_start_loc, seq_lens, block_table, bt_row_stride, num_reqs,
+                                 num_tokens, max_query_len, max_seq_len, num_blocks, a.k_scale,
+                                 a.v_scale, s));
   if (dtype == PKV_BF16)
     return launch_status(pkv::launch_attention_bf16(a, plan, workspace, kv8, s));
   return launch_status(pkv::launch_attention_f32(a, s));

@@ -33,6 +33,23 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
                     int32_t max_seq_len, int32_t split_tokens, pkv_dtype dtype, AttnPlan* plan);
 
+// Device-data checks of the checked build (checks.hip; PKV_DEBUG_CHECKS).
+uint32_t last_check_flags();
+pkv_status check_prepare(const int32_t* nst, const int32_t* nct, const int32_t* block_table,
+                         int64_t bt_stride, int32_t num_reqs, int32_t num_tokens,
+                         int32_t block_size, int64_t num_blocks, hipStream_t stream);
+pkv_status check_slots(const int64_t* slots, int32_t num_tokens, int64_t num_slots,
+                       const float* k_scale, const float* v_scale, hipStream_t stream);
+pkv_status check_attention(const int32_t* qsl, const int32_t* seq_lens,
+                           const int32_t* block_table, int64_t bt_stride, int32_t num_reqs,
+                           int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                           int64_t num_blocks, const float* k_scale, const float* v_scale,
+                           hipStream_t stream);
+pkv_status check_rows(const int32_t* req_indices, const int32_t* positions, int32_t num_tokens,
+                      int32_t num_reqs, int64_t row_width, hipStream_t stream);
+pkv_status check_block_list(const int32_t* ids, int32_t n, bool pairs, int64_t num_blocks,
+                            hipStream_t stream);
+
 hipError_t launch_prepare(const int32_t* nst, const int32_t* nct, const int32_t* block_table,
                           int64_t bt_stride, int32_t num_reqs, int32_t num_tokens,
                           int32_t qsl_len, int32_t block_size, int64_t num_blocks,

@@ -37,9 +37,41 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert binding.status_string(code) != "unknown status"
     assert binding.status_string(99) == "unknown status"
+
+
+def test_checked_build_exports_the_same_symbols():
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.CHECKED_LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pkv_\w+)", out))
+    assert set(declared_functions()) <= exported
+    regular = ctypes.CDLL(binding.REGULAR_LIB_PATH)
+    checked = ctypes.CDLL(binding.CHECKED_LIB_PATH)
+    assert regular.pkv_debug_checks_enabled() == 0
+    assert checked.pkv_debug_checks_enabled() == 1
+    # the checked build keeps the flags of this process's last failed check
+    assert regular.pkv_debug_check_flags() == 0
+
+
+def test_check_bits_match_the_header():
+    text = open(HEADER).read()
+    bits = {m.group(1).lower(): int(m.group(2), 16)
+            for m in re.finditer(r"#define PKV_CHECK_(\w+) (0x[0-9a-f]+)u", text)}
+    assert bits == binding.CHECK_BITS
+
+
+def test_checked_build_validates_host_arguments_first():
+    checked = binding.use_checked(True)
+    try:
+        # host-side rejections come before any device-side check (no GPU needed)
+        assert kvw(checked, T=-1) == binding.ERR_INVALID_ARG
+        assert attn(checked, Hq=6, Hkv=4) == binding.ERR_INVALID_ARG
+        assert block_op(checked, "pkv_zero_blocks", bb=1000) == binding.ERR_UNSUPPORTED
+        assert kvw(checked, T=0, k=None, v=None, slot=None) == binding.OK
+    finally:
+        binding.use_checked(False)
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below returns before launching
