@@ -262,13 +262,24 @@ def kv_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.
     _check(st, "pkv_kv_cache_write_fp8")
 
 
+def split_tokens_or_env(split_tokens: int) -> int:
+    """The context partition size a call uses: the argument, or when it is 0
+    (the library's own choice) the PKV_SPLIT_TOKENS environment variable if set
+    (a multiple of 32; for tuning without touching the caller)."""
+    if split_tokens == 0:
+        env = os.environ.get("PKV_SPLIT_TOKENS", "")
+        if env:
+            return int(env)
+    return int(split_tokens)
+
+
 def attention_workspace_bytes(num_reqs: int, num_tokens: int, num_q_heads: int,
                               num_kv_heads: int, head_dim: int, max_query_len: int,
                               max_seq_len: int, split_tokens: int = 0,
                               dtype: torch.dtype = torch.bfloat16) -> int:
     return int(load().pkv_paged_attention_workspace_bytes(
         num_reqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len, max_seq_len,
-        split_tokens, _dtype_code(dtype)))
+        split_tokens_or_env(split_tokens), _dtype_code(dtype)))
 
 
 def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
@@ -284,6 +295,7 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     float32 device tensors."""
     T, Hq, d = q.shape
     nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    split_tokens = split_tokens_or_env(split_tokens)
     fp8 = k_scale is not None
     if fp8:
         assert v_scale is not None and key_cache.dtype == torch.uint8

@@ -205,3 +205,15 @@ def test_block_ops_empty_is_ok(lib, fn):
 def test_attention_rejects_a_work_list_past_the_dispatch_limit(lib):
     # 32-token partitions of 2^30-token contexts: far more than 2^24 - 1 items
     assert attn(lib, R=1000, T=1000, mq=1, ms=1 << 30, split=32) == binding.ERR_UNSUPPORTED
+
+
+def test_split_tokens_environment_override(monkeypatch):
+    args = (16, 16, 64, 8, 128, 1, 32768)
+    monkeypatch.delenv("PKV_SPLIT_TOKENS", raising=False)
+    forced = binding.attention_workspace_bytes(*args, split_tokens=1024)
+    default = binding.attention_workspace_bytes(*args)
+    assert forced != default
+    monkeypatch.setenv("PKV_SPLIT_TOKENS", "1024")
+    assert binding.attention_workspace_bytes(*args) == forced
+    assert binding.attention_workspace_bytes(*args, split_tokens=32768) != forced  # argument wins
+    assert binding.split_tokens_or_env(0) == 1024 and binding.split_tokens_or_env(64) == 64
