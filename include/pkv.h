@@ -19,6 +19,10 @@
  *                              alike, in one launch) over its request's
  *                              context, read through the block table;
  *   pkv_paged_attention_varlen_fp8  the same over FP8 pools;
+ *   pkv_paged_attention_plan / pkv_paged_attention_run  the attention call in
+ *                              two halves: the work list once per batch,
+ *                              then any number of calls over it (one per
+ *                              model layer);
  *   pkv_copy_blocks            whole-block copies in both pools (copy-on-write
  *                              of a shared block);
  *   pkv_zero_blocks            whole-block clears in both pools (freshly
@@ -100,6 +104,8 @@ typedef enum pkv_status {
 #define PKV_CHECK_PAIRS 0x080u     /* block copies: a destination repeated or also a
                                       source (checked up to 65536 pairs)               */
 #define PKV_CHECK_SCALE 0x100u     /* an FP8 scale not finite and positive             */
+#define PKV_CHECK_PLAN 0x200u      /* pkv_paged_attention_run: the workspace holds no
+                                      work list for these sizes and this batch          */
 
 typedef enum pkv_dtype {
   PKV_F32 = 0,  /* IEEE binary32                                   */
@@ -383,6 +389,51 @@ pkv_status pkv_paged_attention_varlen_fp8(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     float scale, const float* k_scale, const float* v_scale, int32_t split_tokens,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attention_plan, pkv_paged_attention_run -- pkv_paged_attention_varlen
+ * in two halves.  Every layer of a model runs attention over the same batch:
+ * the same query_start_loc, seq_lens, block table and sizes, with its own q,
+ * pools and output.  The plan half derives the call's work list (the order
+ * of prompt tiles and decode partitions) from query_start_loc and seq_lens
+ * into `workspace`; the run half executes attention over that list.  One plan
+ * per batch, then one run per layer, does the same work as one
+ * pkv_paged_attention_varlen per layer without re-deriving the list.
+ *
+ * pkv_paged_attention_plan: arguments as for pkv_paged_attention_varlen
+ * (those it takes); q, pools, table and scale are not needed.  The fp32 path
+ * has no work list: the call then only validates its arguments.
+ * pkv_paged_attention_run: arguments as for pkv_paged_attention_varlen, plus
+ * k_scale and v_scale: both null for 16-bit pools, or both device float32
+ * scalars for FP8 pools (dtype PKV_BF16; see pkv_paged_attention_varlen_fp8).
+ * Precondition: `workspace` holds the work list of a plan (or of a
+ * pkv_paged_attention_varlen* call) made with the same query_start_loc and
+ * seq_lens contents and the same num_reqs, num_tokens, max_query_len,
+ * max_seq_len, num_q_heads, num_kv_heads, head_dim, dtype and split_tokens,
+ * enqueued earlier on the same stream (or ordered before it), with no other
+ * call using the workspace in between.  Runs over one workspace must not
+ * overlap: they share its partition buffers.  The checked build verifies the
+ * list's record of the sizes and a checksum of the batch (PKV_CHECK_PLAN);
+ * the regular build relies on the precondition, and with a stale list the
+ * result is unspecified (the kernels still stay inside their buffers).
+ * Errors: as for pkv_paged_attention_varlen; PKV_ERR_INVALID_ARG when only
+ * one scale is given, or scales with dtype PKV_F32.
+ */
+pkv_status pkv_paged_attention_plan(const int32_t* query_start_loc, const int32_t* seq_lens,
+                                    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len,
+                                    int32_t max_seq_len, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                                    int32_t split_tokens, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_attention_run(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, const float* k_scale, const float* v_scale,
+    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_copy_blocks -- copy-on-write of whole blocks, both pools at once.

@@ -25,12 +25,13 @@ LIB_PATH = CHECKED_LIB_PATH if os.environ.get("PKV_DEBUG_CHECKS") == "1" else RE
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE_DATA = range(6)
 # PKV_CHECK_* bits of the checked build (include/pkv.h)
 CHECK_BITS = {"counts": 0x001, "block_id": 0x002, "slot": 0x004, "slot_dup": 0x008, "qsl": 0x010,
-              "lengths": 0x020, "row": 0x040, "pairs": 0x080, "scale": 0x100}
+              "lengths": 0x020, "row": 0x040, "pairs": 0x080, "scale": 0x100, "plan": 0x200}
 F32, BF16 = 0, 1
 EXPORTS = ("pkv_status_string", "pkv_debug_checks_enabled", "pkv_debug_check_flags",
            "pkv_prepare_inputs", "pkv_prepare_input_ids",
            "pkv_kv_cache_write", "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
-           "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8", "pkv_copy_blocks",
+           "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8",
+           "pkv_paged_attention_plan", "pkv_paged_attention_run", "pkv_copy_blocks",
            "pkv_zero_blocks")
 
 
@@ -84,6 +85,13 @@ def load() -> ctypes.CDLL:
                                                    i32, i32, i32, i32, i32, i32, i32, f32, P, P,
                                                    i32, P, sz, P]
     lib.pkv_paged_attention_varlen_fp8.restype = ctypes.c_int
+    lib.pkv_paged_attention_plan.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int,
+                                             i32, P, sz, P]
+    lib.pkv_paged_attention_plan.restype = ctypes.c_int
+    lib.pkv_paged_attention_run.argtypes = [P, i64, P, P, i64, P, i64, P, P, P, i64, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, f32, ctypes.c_int, P, P, i32,
+                                            P, sz, P]
+    lib.pkv_paged_attention_run.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -193,6 +201,31 @@ def prepare_input_ids(token_table: torch.Tensor, req_indices: torch.Tensor,
     return out
 
 
+def paged_attention_plan(query_start_loc: torch.Tensor, seq_lens: torch.Tensor, *,
+                         num_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                         max_query_len: int, max_seq_len: int,
+                         dtype: torch.dtype = torch.bfloat16, split_tokens: int = 0,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """pkv_paged_attention_plan: the batch's work list in ``workspace``
+    (allocated when not given); pass it to paged_attention(..., planned=True,
+    workspace=...) once per layer.  dtype is the q dtype (bf16 also for FP8
+    pools)."""
+    R = int(seq_lens.shape[0])
+    split_tokens = split_tokens_or_env(split_tokens)
+    need = attention_workspace_bytes(R, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                     max_query_len, max_seq_len, split_tokens, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=seq_lens.device)
+    st = load().pkv_paged_attention_plan(
+        _dev(query_start_loc, torch.int32, "query_start_loc"),
+        _dev(seq_lens, torch.int32, "seq_lens"), R, int(num_tokens), int(max_query_len),
+        int(max_seq_len), int(num_q_heads), int(num_kv_heads), int(head_dim), _dtype_code(dtype),
+        int(split_tokens), _dev(workspace, name="workspace"),
+        workspace.numel() * workspace.element_size(), _stream(seq_lens.device))
+    _check(st, "pkv_paged_attention_plan")
+    return workspace
+
+
 def _pool_block_bytes(key_cache: torch.Tensor, value_cache: torch.Tensor) -> int:
     assert key_cache.is_contiguous() and value_cache.is_contiguous()
     assert key_cache.shape[0] == value_cache.shape[0] and key_cache.dtype == value_cache.dtype
@@ -288,11 +321,12 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                     scale: float | None = None, out: torch.Tensor | None = None,
                     split_tokens: int = 0, workspace: torch.Tensor | None = None,
                     k_scale: torch.Tensor | None = None,
-                    v_scale: torch.Tensor | None = None) -> torch.Tensor:
+                    v_scale: torch.Tensor | None = None, planned: bool = False) -> torch.Tensor:
     """pkv_paged_attention_varlen (or _fp8 when k_scale / v_scale are given).
     q: [T, Hq, d]; 16-bit pools: K [nb, Hkv, 16, d], V [nb, Hkv, d, 16]; FP8
     pools (uint8): K [nb, Hkv, 16, d], V [nb, Hkv, d * 16]; scales: one-element
-    float32 device tensors."""
+    float32 device tensors.  planned=True: pkv_paged_attention_run over the work
+    list a paged_attention_plan call left in ``workspace``."""
     T, Hq, d = q.shape
     nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
     split_tokens = split_tokens_or_env(split_tokens)
@@ -310,6 +344,7 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     need = attention_workspace_bytes(R, T, Hq, Hkv, d, max_query_len, max_seq_len, split_tokens,
                                      q.dtype)
     if workspace is None and need:
+        assert not planned, "a planned call runs over the plan's workspace"
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, name="workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -321,6 +356,13 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                  _dev(seq_lens, torch.int32, "seq_lens"),
                  _dev(block_table, torch.int32, "block_table"), block_table.stride(0), R, T,
                  int(max_query_len), int(max_seq_len), Hq, Hkv, d, bs, float(scale))
+    if planned:
+        st = load().pkv_paged_attention_run(
+            *args_head, BF16 if fp8 else _dtype_code(q.dtype),
+            _dev(k_scale, torch.float32, "k_scale"), _dev(v_scale, torch.float32, "v_scale"),
+            int(split_tokens), ws_ptr, ws_bytes, _stream(q.device))
+        _check(st, "pkv_paged_attention_run")
+        return out
     if fp8:
         st = load().pkv_paged_attention_varlen_fp8(
             *args_head, _dev(k_scale, torch.float32, "k_scale"),

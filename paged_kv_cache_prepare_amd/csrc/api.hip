@@ -209,23 +209,41 @@ pkv_status pkv_zero_blocks(void* key_cache, void* value_cache, int64_t num_block
 
 }  // extern "C"
 
+// What an attention call does: plan and run (pkv_paged_attention_varlen*),
+// or one of the two (pkv_paged_attention_plan / pkv_paged_attention_run).
+enum class AttnMode { kFused, kPlan, kRun };
+
+// FNV-1a over the sizes a work list depends on.
+static uint32_t plan_fingerprint(const pkv::AttnPlan& plan, int32_t num_reqs, int32_t num_tokens,
+                                 int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim) {
+  const int64_t v[] = {num_reqs,     num_tokens, max_query_len,      max_seq_len, num_q_heads,
+                       num_kv_heads, head_dim,   plan.split_tokens, plan.max_splits};
+  uint32_t h = 2166136261u;
+  for (int64_t x : v)
+    for (int k = 0; k < 8; ++k) h = (h ^ (uint32_t)((x >> (8 * k)) & 0xff)) * 16777619u;
+  return h;
+}
+
 static pkv_status attention_call(
-    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
-    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
-    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
-    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
-    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    float scale, pkv_dtype dtype, const float* k_scale, const float* v_scale,
-    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    AttnMode mode, const void* q, int64_t q_row_stride, const void* key_cache,
+    const void* value_cache, int64_t num_blocks, void* out, int64_t out_row_stride,
+    const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* block_table,
+    int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens, int32_t max_query_len,
+    int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, pkv_dtype dtype, const float* k_scale,
+    const float* v_scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+    void* stream) {
   const bool kv8 = k_scale != nullptr;
+  const bool runs = mode != AttnMode::kPlan;
   if (num_reqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0 ||
       num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
       split_tokens < 0 || split_tokens % 32 != 0)
     return PKV_ERR_INVALID_ARG;
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
-  if (!(scale > 0.f) || scale == HUGE_VALF) return PKV_ERR_INVALID_ARG;  // also rejects NaN
+  if (runs && (!(scale > 0.f) || scale == HUGE_VALF)) return PKV_ERR_INVALID_ARG;  // and NaN
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
-  if (block_size != pkv::kBlock) return PKV_ERR_UNSUPPORTED;
+  if (runs && block_size != pkv::kBlock) return PKV_ERR_UNSUPPORTED;
   const int32_t group = num_q_heads / num_kv_heads;
   if (dtype == PKV_BF16 && group > pkv::kPairsPerTile) return PKV_ERR_UNSUPPORTED;
   if (num_q_heads > 65535) return PKV_ERR_UNSUPPORTED;
@@ -235,18 +253,20 @@ static pkv_status attention_call(
     return PKV_ERR_INVALID_ARG;
   if (plan.max_items > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;  // one workgroup per item
   if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
-  if (!q || !key_cache || !value_cache || !out || !query_start_loc || !seq_lens || !block_table)
-    return PKV_ERR_INVALID_ARG;
-  if (kv8 && (!v_scale || (reinterpret_cast<uintptr_t>(k_scale) & 3) != 0 ||
-              (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0))
-    return PKV_ERR_INVALID_ARG;
-  const int64_t row = (int64_t)num_q_heads * head_dim;
+  if (!query_start_loc || !seq_lens) return PKV_ERR_INVALID_ARG;
   const int32_t esz = dtype == PKV_BF16 ? 2 : 4;
-  if (q_row_stride < row || out_row_stride < row || bt_row_stride < 1 || num_blocks < 1)
-    return PKV_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(key_cache) || !aligned16(value_cache) ||
-      q_row_stride * esz % 16 != 0 || out_row_stride * esz % 16 != 0)
-    return PKV_ERR_INVALID_ARG;
+  if (runs) {
+    if (!q || !key_cache || !value_cache || !out || !block_table) return PKV_ERR_INVALID_ARG;
+    if (kv8 && (!v_scale || (reinterpret_cast<uintptr_t>(k_scale) & 3) != 0 ||
+                (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0))
+      return PKV_ERR_INVALID_ARG;
+    const int64_t row = (int64_t)num_q_heads * head_dim;
+    if (q_row_stride < row || out_row_stride < row || bt_row_stride < 1 || num_blocks < 1)
+      return PKV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        q_row_stride * esz % 16 != 0 || out_row_stride * esz % 16 != 0)
+      return PKV_ERR_INVALID_ARG;
+  }
   if (plan.total_bytes > 0 &&
       (workspace == nullptr || workspace_bytes < plan.total_bytes ||
        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
@@ -273,14 +293,26 @@ static pkv_status attention_call(
   a.k_scale = kv8 ? k_scale : nullptr;
   a.v_scale = kv8 ? v_scale : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  PKV_CHECK(pkv::check_attention(query_start_loc, seq_lens, block_table, bt_row_stride, num_reqs,
-                                 num_tokens, max_query_len, max_seq_len, num_blocks, a.k_scale,
-                                 a.v_scale, s));
-  if (dtype == PKV_BF16)
-    return launch_status(pkv::launch_attention_bf16(a, plan, workspace, kv8, s));
+  const uint32_t fp = plan_fingerprint(plan, num_reqs, num_tokens, max_query_len, max_seq_len,
+                                       num_q_heads, num_kv_heads, head_dim);
+  // a run over a work list made earlier: a checked build compares its record
+  const int32_t* planned =
+      mode == AttnMode::kRun && plan.total_bytes > 0 ? static_cast<const int32_t*>(workspace)
+                                                     : nullptr;
+  PKV_CHECK(pkv::check_attention(query_start_loc, seq_lens, runs ? block_table : nullptr,
+                                 bt_row_stride, num_reqs, num_tokens, max_query_len, max_seq_len,
+                                 num_blocks, a.k_scale, a.v_scale, planned, fp, s));
+  if (dtype == PKV_BF16) {
+    if (mode != AttnMode::kRun) {
+      const hipError_t e = pkv::launch_attention_plan(a, plan, workspace, fp, s);
+      if (e != hipSuccess) return launch_status(e);
+    }
+    if (!runs) return PKV_OK;
+    return launch_status(pkv::launch_attention_run(a, plan, workspace, kv8, s));
+  }
+  if (!runs) return PKV_OK;  // the fp32 path has no work list
   return launch_status(pkv::launch_attention_f32(a, s));
 }
-
 
 extern "C" {
 
@@ -292,11 +324,11 @@ pkv_status pkv_paged_attention_varlen(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     float scale, pkv_dtype dtype, int32_t split_tokens, void* workspace,
     size_t workspace_bytes, void* stream) {
-  return attention_call(q, q_row_stride, key_cache, value_cache, num_blocks, out, out_row_stride,
-                        query_start_loc, seq_lens, block_table, bt_row_stride, num_reqs,
-                        num_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads,
-                        head_dim, block_size, scale, dtype, nullptr, nullptr, split_tokens,
-                        workspace, workspace_bytes, stream);
+  return attention_call(AttnMode::kFused, q, q_row_stride, key_cache, value_cache, num_blocks,
+                        out, out_row_stride, query_start_loc, seq_lens, block_table,
+                        bt_row_stride, num_reqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, nullptr,
+                        nullptr, split_tokens, workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_paged_attention_varlen_fp8(
@@ -308,11 +340,41 @@ pkv_status pkv_paged_attention_varlen_fp8(
     float scale, const float* k_scale, const float* v_scale, int32_t split_tokens,
     void* workspace, size_t workspace_bytes, void* stream) {
   if (!k_scale || !v_scale) return PKV_ERR_INVALID_ARG;
-  return attention_call(q, q_row_stride, key_cache, value_cache, num_blocks, out, out_row_stride,
-                        query_start_loc, seq_lens, block_table, bt_row_stride, num_reqs,
-                        num_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads,
-                        head_dim, block_size, scale, PKV_BF16, k_scale, v_scale, split_tokens,
-                        workspace, workspace_bytes, stream);
+  return attention_call(AttnMode::kFused, q, q_row_stride, key_cache, value_cache, num_blocks,
+                        out, out_row_stride, query_start_loc, seq_lens, block_table,
+                        bt_row_stride, num_reqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, scale, PKV_BF16,
+                        k_scale, v_scale, split_tokens, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_plan(const int32_t* query_start_loc, const int32_t* seq_lens,
+                                    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len,
+                                    int32_t max_seq_len, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                                    int32_t split_tokens, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return attention_call(AttnMode::kPlan, nullptr, 0, nullptr, nullptr, 0, nullptr, 0,
+                        query_start_loc, seq_lens, nullptr, 0, num_reqs, num_tokens,
+                        max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                        pkv::kBlock, 1.f, dtype, nullptr, nullptr, split_tokens, workspace,
+                        workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_run(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, const float* k_scale, const float* v_scale,
+    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if ((k_scale == nullptr) != (v_scale == nullptr)) return PKV_ERR_INVALID_ARG;
+  if (k_scale != nullptr && dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  return attention_call(AttnMode::kRun, q, q_row_stride, key_cache, value_cache, num_blocks,
+                        out, out_row_stride, query_start_loc, seq_lens, block_table,
+                        bt_row_stride, num_reqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, k_scale,
+                        v_scale, split_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

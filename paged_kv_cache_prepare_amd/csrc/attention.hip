@@ -233,11 +233,21 @@ __device__ inline int plan_units(const int32_t* qsl, const int32_t* seq_lens, in
 __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t num_reqs,
     int32_t num_tokens, int32_t num_kv_heads, int32_t group, int32_t split_tokens, int32_t max_splits,
-    int64_t max_items, int4* __restrict__ items, int32_t* __restrict__ n_items) {
+    int64_t max_items, int4* __restrict__ items, int32_t* __restrict__ n_items,
+    uint32_t fingerprint) {
   __shared__ PlanSmem sm;
+  __shared__ uint32_t batch_sum;
   const int tid = threadIdx.x;
   const int H = num_kv_heads;
   int64_t carry = 0;  // units emitted so far; item index = unit * H + kv head
+  // a checksum of the batch the list is made for (plan_batch_term), word 2
+  if (tid == 0) batch_sum = 0u;
+  __syncthreads();
+  {
+    uint32_t part = tid == 0 ? (uint32_t)qsl[0] * 374761393u : 0u;
+    for (int r = tid; r < num_reqs; r += kPlanReqs) part += plan_batch_term(r, qsl[r + 1], seq_lens[r]);
+    atomicAdd(&batch_sum, part);
+  }
   const bool ordered = num_reqs <= kPlanReqs && max_splits <= kPlanMaxSplits;
 
   if (ordered) {
@@ -349,6 +359,10 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
   if (tid == 0) {
     const int64_t n = carry * H;
     *n_items = (int32_t)(n < max_items ? n : max_items);
+    // the sizes and the batch the list was made for, so that a checked run
+    // can tell
+    n_items[1] = (int32_t)fingerprint;
+    n_items[2] = (int32_t)batch_sum;
   }
 }
 
@@ -1545,20 +1559,28 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int32_t group)
   for (int k = 0; k < PER; ++k) out[lane + 64 * k] = o[k] * inv;
 }
 
+// The work list: item count at workspace word 0, the plan fingerprint at
+// word 1, items from plan.items_offset.
+hipError_t launch_plan(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                       uint32_t fingerprint, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanReqs), 0, stream, a.qsl, a.seq_lens,
+                     a.num_reqs, a.num_tokens, a.num_kv_heads, plan.group, plan.split_tokens,
+                     plan.max_splits, plan.max_items, reinterpret_cast<int4*>(ws + plan.items_offset),
+                     reinterpret_cast<int32_t*>(ws), fingerprint);
+  return hipGetLastError();
+}
+
 template <int D, bool KV8>
-hipError_t launch_bf16_d(const AttnArgs& a, const AttnPlan& plan, void* workspace,
-                         hipStream_t stream) {
+hipError_t launch_run_d(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                        hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   int32_t* n_items = reinterpret_cast<int32_t*>(ws);
   int4* items = reinterpret_cast<int4*>(ws + plan.items_offset);
   float* ml = plan.max_splits > 1 ? reinterpret_cast<float*>(ws + plan.ml_offset) : nullptr;
   float* opart = plan.max_splits > 1 ? reinterpret_cast<float*>(ws + plan.o_offset) : nullptr;
   const float c2 = a.scale * kLog2e;
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanReqs), 0, stream, a.qsl, a.seq_lens,
-                     a.num_reqs, a.num_tokens, a.num_kv_heads, plan.group, plan.split_tokens, plan.max_splits,
-                     plan.max_items, items, n_items);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (plan.max_items > 0) {
     hipLaunchKernelGGL((attn_main_kernel<D, KV8>), dim3((unsigned)plan.max_items), dim3(kThreads), 0,
                        stream, a, plan.group, c2, items, n_items, plan.max_splits, ml, opart);
@@ -1628,15 +1650,21 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
   return true;
 }
 
-hipError_t launch_attention_bf16(const AttnArgs& a, const AttnPlan& plan, void* workspace,
-                                 bool kv8, hipStream_t stream) {
+hipError_t launch_attention_plan(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                                 uint32_t fingerprint, hipStream_t stream) {
+  if (a.num_tokens == 0 || a.num_reqs == 0) return hipSuccess;
+  return launch_plan(a, plan, workspace, fingerprint, stream);
+}
+
+hipError_t launch_attention_run(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                                bool kv8, hipStream_t stream) {
   if (a.num_tokens == 0 || a.num_reqs == 0) return hipSuccess;
   if (kv8) {
-    if (a.head_dim == 128) return launch_bf16_d<128, true>(a, plan, workspace, stream);
-    return launch_bf16_d<64, true>(a, plan, workspace, stream);
+    if (a.head_dim == 128) return launch_run_d<128, true>(a, plan, workspace, stream);
+    return launch_run_d<64, true>(a, plan, workspace, stream);
   }
-  if (a.head_dim == 128) return launch_bf16_d<128, false>(a, plan, workspace, stream);
-  return launch_bf16_d<64, false>(a, plan, workspace, stream);
+  if (a.head_dim == 128) return launch_run_d<128, false>(a, plan, workspace, stream);
+  return launch_run_d<64, false>(a, plan, workspace, stream);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {

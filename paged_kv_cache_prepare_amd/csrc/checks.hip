@@ -80,11 +80,19 @@ __global__ __launch_bounds__(256) void check_slots_kernel(const int64_t* slots, 
 
 // query_start_loc, the lengths, and every block-table entry a request's
 // context reads (columns below ceil(seq_len / 16)).  One workgroup per request.
+// A run call (plan != null) also compares the work list's recorded sizes and
+// batch checksum with this call's (workgroup 0, serially).
 __global__ __launch_bounds__(256) void check_attention_kernel(
     const int32_t* qsl, const int32_t* seq_lens, const int32_t* block_table, int64_t bt_stride,
     int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
-    int64_t num_blocks, const float* k_scale, const float* v_scale) {
+    int64_t num_blocks, const float* k_scale, const float* v_scale, const int32_t* plan,
+    uint32_t fingerprint) {
   const int r = blockIdx.x;
+  if (r == 0 && threadIdx.x == 0 && plan != nullptr) {
+    uint32_t sum = (uint32_t)qsl[0] * 374761393u;
+    for (int k = 0; k < num_reqs; ++k) sum += plan_batch_term(k, qsl[k + 1], seq_lens[k]);
+    if ((uint32_t)plan[1] != fingerprint || (uint32_t)plan[2] != sum) flag(PKV_CHECK_PLAN);
+  }
   const int q0 = qsl[r], q1 = qsl[r + 1];
   const int L = seq_lens[r];
   if (threadIdx.x == 0) {
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(256) void check_attention_kernel(
       flag(PKV_CHECK_LENGTHS);
     if (r == 0 && k_scale != nullptr) check_scales(k_scale, v_scale);
   }
-  if (q1 <= q0 || L <= 0) return;  // a request without rows reads nothing
+  if (q1 <= q0 || L <= 0 || block_table == nullptr) return;  // nothing to read
   const int64_t cols = ((int64_t)L + kBlock - 1) / kBlock;
   if (cols > bt_stride && threadIdx.x == 0) flag(PKV_CHECK_BLOCK_ID);
   const int64_t lim = cols < bt_stride ? cols : bt_stride;
@@ -192,12 +200,13 @@ pkv_status check_attention(const int32_t* qsl, const int32_t* seq_lens,
                            const int32_t* block_table, int64_t bt_stride, int32_t num_reqs,
                            int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
                            int64_t num_blocks, const float* k_scale, const float* v_scale,
-                           hipStream_t stream) {
+                           const int32_t* plan, uint32_t fingerprint, hipStream_t stream) {
   if (num_reqs == 0) return PKV_OK;
   return run_check(stream, [&] {
     hipLaunchKernelGGL(check_attention_kernel, dim3((unsigned)num_reqs), dim3(256), 0, stream,
                        qsl, seq_lens, block_table, bt_stride, num_reqs, num_tokens,
-                       max_query_len, max_seq_len, num_blocks, k_scale, v_scale);
+                       max_query_len, max_seq_len, num_blocks, k_scale, v_scale, plan,
+                       fingerprint);
   });
 }
 

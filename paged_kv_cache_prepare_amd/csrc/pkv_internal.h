@@ -33,6 +33,14 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
                     int32_t max_seq_len, int32_t split_tokens, pkv_dtype dtype, AttnPlan* plan);
 
+// One request's term of the batch checksum a work list records (summed mod
+// 2^32 with qsl[0] * 374761393 over the requests).
+__host__ __device__ inline uint32_t plan_batch_term(int32_t r, int32_t qsl_next, int32_t seq_len) {
+  uint32_t t = (uint32_t)qsl_next * 2654435761u + (uint32_t)seq_len * 2246822519u +
+               (uint32_t)r * 3266489917u;
+  return t ^ (t >> 15);
+}
+
 // Device-data checks of the checked build (checks.hip; PKV_DEBUG_CHECKS).
 uint32_t last_check_flags();
 pkv_status check_prepare(const int32_t* nst, const int32_t* nct, const int32_t* block_table,
@@ -40,11 +48,14 @@ pkv_status check_prepare(const int32_t* nst, const int32_t* nct, const int32_t* 
                          int32_t block_size, int64_t num_blocks, hipStream_t stream);
 pkv_status check_slots(const int64_t* slots, int32_t num_tokens, int64_t num_slots,
                        const float* k_scale, const float* v_scale, hipStream_t stream);
+// block_table may be null (a plan call: nothing reads it).  With `plan`
+// non-null (a run call), the work list's recorded fingerprint and batch
+// checksum must match `fingerprint` and the batch.
 pkv_status check_attention(const int32_t* qsl, const int32_t* seq_lens,
                            const int32_t* block_table, int64_t bt_stride, int32_t num_reqs,
                            int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
                            int64_t num_blocks, const float* k_scale, const float* v_scale,
-                           hipStream_t stream);
+                           const int32_t* plan, uint32_t fingerprint, hipStream_t stream);
 pkv_status check_rows(const int32_t* req_indices, const int32_t* positions, int32_t num_tokens,
                       int32_t num_reqs, int64_t row_width, hipStream_t stream);
 pkv_status check_block_list(const int32_t* ids, int32_t n, bool pairs, int64_t num_blocks,
@@ -110,8 +121,12 @@ struct AttnArgs {
 };
 
 // bf16 queries; kv8 selects FP8 E4M3 pools (a.k_scale / a.v_scale set).
-hipError_t launch_attention_bf16(const AttnArgs& a, const AttnPlan& plan, void* workspace,
-                                 bool kv8, hipStream_t stream);
+// bf16 path: the work list (plan), then the main and reduce kernels over it
+// (run); `fingerprint` identifies the sizes the list was made for.
+hipError_t launch_attention_plan(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                                 uint32_t fingerprint, hipStream_t stream);
+hipError_t launch_attention_run(const AttnArgs& a, const AttnPlan& plan, void* workspace,
+                                bool kv8, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace pkv

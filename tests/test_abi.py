@@ -217,3 +217,45 @@ def test_split_tokens_environment_override(monkeypatch):
     assert binding.attention_workspace_bytes(*args) == forced
     assert binding.attention_workspace_bytes(*args, split_tokens=32768) != forced  # argument wins
     assert binding.split_tokens_or_env(0) == 1024 and binding.split_tokens_or_env(64) == 64
+
+
+def plan(lib, **kw):
+    a = dict(qsl=FAKE, sl=FAKE, R=3, T=10, mq=5, ms=100, Hq=4, Hkv=2, d=128, dt=binding.BF16,
+             split=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pkv_paged_attention_plan(a["qsl"], a["sl"], a["R"], a["T"], a["mq"], a["ms"],
+                                        a["Hq"], a["Hkv"], a["d"], a["dt"], a["split"], a["ws"],
+                                        a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), binding.ERR_INVALID_ARG), (dict(split=48), binding.ERR_INVALID_ARG),
+    (dict(d=96), binding.ERR_UNSUPPORTED), (dict(qsl=None), binding.ERR_INVALID_ARG),
+    (dict(), binding.ERR_WORKSPACE), (dict(ws=FAKE + 16, wsb=1 << 30), binding.ERR_WORKSPACE)])
+def test_plan_rejects(lib, kw, code):
+    assert plan(lib, **kw) == code
+
+
+def test_plan_without_work_is_ok(lib):
+    assert plan(lib, T=0, R=0, qsl=None, sl=None) == binding.OK
+    assert plan(lib, dt=binding.F32) == binding.OK   # the fp32 path keeps no work list
+
+
+def run(lib, **kw):
+    a = dict(q=FAKE, qs=4 * 128, kc=FAKE, vc=FAKE, nb=16, out=FAKE, os=4 * 128, qsl=FAKE,
+             sl=FAKE, bt=FAKE, bts=8, R=3, T=10, mq=5, ms=100, Hq=4, Hkv=2, d=128, bs=16,
+             scale=0.1, dt=binding.BF16, ks=None, vs=None, split=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pkv_paged_attention_run(
+        a["q"], a["qs"], a["kc"], a["vc"], a["nb"], a["out"], a["os"], a["qsl"], a["sl"],
+        a["bt"], a["bts"], a["R"], a["T"], a["mq"], a["ms"], a["Hq"], a["Hkv"], a["d"], a["bs"],
+        a["scale"], a["dt"], a["ks"], a["vs"], a["split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=FAKE), binding.ERR_INVALID_ARG), (dict(ks=FAKE, vs=FAKE, dt=binding.F32),
+                                                binding.ERR_INVALID_ARG),
+    (dict(bt=None), binding.ERR_INVALID_ARG), (dict(scale=0.0), binding.ERR_INVALID_ARG),
+    (dict(bs=32), binding.ERR_UNSUPPORTED), (dict(), binding.ERR_WORKSPACE)])
+def test_run_rejects(lib, kw, code):
+    assert run(lib, **kw) == code

@@ -1,0 +1,142 @@
+"""pkv_paged_attention_plan / pkv_paged_attention_run: one work list per
+batch, then one run per model layer.  Every run must equal, bit for bit, the
+one-call pkv_paged_attention_varlen* on the same inputs (the same kernels over
+the same list), for 16-bit and FP8 pools; a new plan in the same workspace
+serves a new batch; the checked build rejects a run over a list made for
+another batch."""
+import pytest
+import torch
+
+import paged_kv_cache_prepare_amd as pkv
+from paged_kv_cache_prepare_amd import binding, workloads
+
+from gpu_helpers import (assert_attention_close, bits_view, device, gpu_prepare, gpu_scales,
+                         log, oracle_step)
+
+pytestmark = pytest.mark.gpu
+
+NST, NCT = [1, 1, 70, 3, 1, 1], [900, 40, 100, 20, 2000, 333]
+
+
+def _layers(n, fp8=False, nst=NST, nct=NCT):
+    """n layers of one batch: the same token counts, each layer its own seeded
+    q, K/V rows, pools and block placement."""
+    out = []
+    for k in range(n):
+        wl = workloads.build(f"layer{k}", nst, nct, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                             seed=300 + k, device=device(), pool_slack=1.2)
+        out.append(workloads.to_fp8(wl, 0.0125, 0.02) if fp8 else wl)
+    return out
+
+
+def _write(wl):
+    prep, bt = gpu_prepare(wl)
+    kc, vc = wl.key_cache.clone(), wl.value_cache.clone()
+    ks, vs = gpu_scales(wl)
+    if ks is None:
+        pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"], block_size=16)
+    else:
+        pkv.kv_cache_write_fp8(wl.key, wl.value, kc, vc, prep["slot_mapping"], ks, vs,
+                               block_size=16)
+    return prep, bt, kc, vc, ks, vs
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("split", [64, 0])
+def test_one_plan_many_layers(fp8, split):
+    layers = _layers(3, fp8)
+    wl0 = layers[0]
+    prep0, *_ = _write(wl0)
+    ws = pkv.paged_attention_plan(prep0["query_start_loc"], prep0["seq_lens"],
+                                  num_tokens=wl0.num_tokens, num_q_heads=16, num_kv_heads=4,
+                                  head_dim=128, max_query_len=wl0.max_query_len,
+                                  max_seq_len=wl0.max_seq_len, split_tokens=split)
+    for k, wl in enumerate(layers):
+        prep, bt, kc, vc, ks, vs = _write(wl)
+        kw = dict(max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, scale=wl.scale,
+                  split_tokens=split, k_scale=ks, v_scale=vs)
+        # qsl / seq_lens of this layer hold the same values the plan was made from
+        run = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                                  planned=True, workspace=ws, **kw)
+        run = run.clone()
+        fused = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                                    **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(bits_view(run), bits_view(fused)), f"layer {k}"
+        if k == 2:
+            _, _, _, ref = oracle_step(wl)
+            assert_attention_close(run, ref, wl.dtype, f"planned layer {k}")
+        log(f"  layer {k}: run over the shared plan equals the one-call attention")
+
+
+def test_replanning_the_workspace_for_a_new_batch():
+    a = _layers(1)[0]
+    b = _layers(1, nst=[1, 1, 1, 40], nct=[5000, 17, 260, 0])[0]
+    prep_a, bt_a, kc_a, vc_a, _, _ = _write(a)
+    prep_b, bt_b, kc_b, vc_b, _, _ = _write(b)
+    # a workspace large enough for both batches
+    size = max(pkv.attention_workspace_bytes(w.num_reqs, w.num_tokens, 16, 4, 128,
+                                             w.max_query_len, w.max_seq_len, 64)
+               for w in (a, b))
+    ws = torch.empty(size, dtype=torch.uint8, device=device())
+    for wl, prep, bt, kc, vc in ((a, prep_a, bt_a, kc_a, vc_a), (b, prep_b, bt_b, kc_b, vc_b),
+                                 (a, prep_a, bt_a, kc_a, vc_a)):
+        pkv.paged_attention_plan(prep["query_start_loc"], prep["seq_lens"],
+                                 num_tokens=wl.num_tokens, num_q_heads=16, num_kv_heads=4,
+                                 head_dim=128, max_query_len=wl.max_query_len,
+                                 max_seq_len=wl.max_seq_len, split_tokens=64, workspace=ws)
+        kw = dict(max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, scale=wl.scale,
+                  split_tokens=64)
+        run = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                                  planned=True, workspace=ws, **kw).clone()
+        fused = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                                    **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(bits_view(run), bits_view(fused))
+
+
+def test_fp32_plan_is_a_no_op_and_run_works():
+    wl = workloads.config(1, device=device())
+    prep, bt, kc, vc, _, _ = _write(wl)
+    ws = pkv.paged_attention_plan(prep["query_start_loc"], prep["seq_lens"],
+                                  num_tokens=wl.num_tokens, num_q_heads=4, num_kv_heads=2,
+                                  head_dim=64, max_query_len=wl.max_query_len,
+                                  max_seq_len=wl.max_seq_len, dtype=torch.float32)
+    kw = dict(max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, scale=wl.scale)
+    run = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                              planned=True, workspace=ws, **kw).clone()
+    fused = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(bits_view(run), bits_view(fused))
+
+
+def test_checked_build_rejects_a_stale_plan():
+    a = _layers(1)[0]
+    b = _layers(1, nst=[1, 2, 1, 1, 1, 1], nct=NCT)[0]   # the same requests, other counts
+    prep_a, bt_a, kc_a, vc_a, _, _ = _write(a)
+    prep_b, *_ = _write(b)
+    binding.use_checked(True)
+    try:
+        size = max(pkv.attention_workspace_bytes(w.num_reqs, w.num_tokens, 16, 4, 128,
+                                                 w.max_query_len, w.max_seq_len, 64)
+                   for w in (a, b))
+        ws = torch.empty(size, dtype=torch.uint8, device=device())
+        kw = dict(max_query_len=a.max_query_len, max_seq_len=a.max_seq_len, scale=a.scale,
+                  split_tokens=64)
+        pkv.paged_attention_plan(prep_b["query_start_loc"], prep_b["seq_lens"],
+                                 num_tokens=b.num_tokens, num_q_heads=16, num_kv_heads=4,
+                                 head_dim=128, max_query_len=b.max_query_len,
+                                 max_seq_len=b.max_seq_len, split_tokens=64, workspace=ws)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.paged_attention(a.q, kc_a, vc_a, prep_a["query_start_loc"], prep_a["seq_lens"],
+                                bt_a, planned=True, workspace=ws, **kw)
+        assert e.value.status == binding.ERR_DEVICE_DATA and "plan" in binding.check_flags()
+        pkv.paged_attention_plan(prep_a["query_start_loc"], prep_a["seq_lens"],
+                                 num_tokens=a.num_tokens, num_q_heads=16, num_kv_heads=4,
+                                 head_dim=128, max_query_len=a.max_query_len,
+                                 max_seq_len=a.max_seq_len, split_tokens=64, workspace=ws)
+        pkv.paged_attention(a.q, kc_a, vc_a, prep_a["query_start_loc"], prep_a["seq_lens"], bt_a,
+                            planned=True, workspace=ws, **kw)
+        torch.cuda.synchronize()
+    finally:
+        binding.use_checked(False)
