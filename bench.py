@@ -461,6 +461,19 @@ def main():
     torch.cuda.synchronize(dev)
     t_prep = float(np.mean([e[0].elapsed_time(e[1]) for e in ph_ev]))
     t_write = float(np.mean([p[1].elapsed_time(a[0]) for p, a in zip(ph_ev, at_ev)]))
+    # the attention call without its planning step (pkv_paged_attention_run over
+    # the work list the last step left in the workspace): what each further
+    # layer of a model pays for the same batch
+    run_ev = new_events(phase_steps, 2)
+    for k in range(phase_steps):
+        run_ev[k][0].record(stream)
+        pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                            scale=wl.scale, out=out, split_tokens=args.split_tokens,
+                            workspace=ws, k_scale=ks, v_scale=vs, planned=True)
+        run_ev[k][1].record(stream)
+    torch.cuda.synchronize(dev)
+    t_run = float(np.mean([e[0].elapsed_time(e[1]) for e in run_ev]))
 
     graph_ms = None
     if args.graph:
@@ -524,8 +537,10 @@ def main():
                    "kv_dtype": args.kv_dtype},
         "phases_ms": {"prepare": round(t_prep, 4), "kv_write": round(t_write, 4),
                       "attention": round(t_attn, 4),
-                      "note": "attention from events in the timed region; prepare and "
-                              "kv_write from a separate pass of event-bracketed steps"},
+                      "attention_run_only": round(t_run, 4),
+                      "note": "attention from events in the timed region; prepare, kv_write "
+                              "and attention_run_only (the call without re-planning, as every "
+                              "further layer of a model step runs it) from separate passes"},
         "context_tokens_per_s": round(work["context_tokens"] / (ms_step / 1e3), 1),
         "attention_hbm_gbs": round(gbs, 1),
         "attention_tflops": round(tflops, 3),
