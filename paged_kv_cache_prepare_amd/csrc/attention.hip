@@ -223,8 +223,9 @@ __device__ inline int plan_units(const int32_t* qsl, const int32_t* seq_lens, in
 // head.  Prefill units come first, then decode units.
 //
 // Ordered path (num_reqs <= kPlanReqs and max_splits <= kPlanMaxSplits):
-// requests are ranked by seq_len, longest first, so the longest work starts
-// first and the tail of the launch holds the short items.  Prefill tiles of a
+// requests are ranked by seq_len (to 1/1024 of the longest), longest first, so
+// the longest work starts first and the tail of the launch holds the short
+// items.  Prefill tiles of a
 // request go latest rows first (they see the most keys).  Decode units go
 // partition-major: partition 0 of every request, then partition 1, ...; the
 // later partitions of a context are its shorter remainders, and requests that
@@ -237,36 +238,59 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     uint32_t fingerprint) {
   __shared__ PlanSmem sm;
   __shared__ uint32_t batch_sum;
+  __shared__ int max_len;
   const int tid = threadIdx.x;
   const int H = num_kv_heads;
   int64_t carry = 0;  // units emitted so far; item index = unit * H + kv head
   // a checksum of the batch the list is made for (plan_batch_term), word 2
-  if (tid == 0) batch_sum = 0u;
-  __syncthreads();
-  {
-    uint32_t part = tid == 0 ? (uint32_t)qsl[0] * 374761393u : 0u;
-    for (int r = tid; r < num_reqs; r += kPlanReqs) part += plan_batch_term(r, qsl[r + 1], seq_lens[r]);
-    atomicAdd(&batch_sum, part);
+  if (tid == 0) {
+    batch_sum = 0u;
+    max_len = 0;
   }
+  __syncthreads();
   const bool ordered = num_reqs <= kPlanReqs && max_splits <= kPlanMaxSplits;
 
   if (ordered) {
     // every per-request input is read once, up front, in one round trip
-    const int L = tid < num_reqs ? seq_lens[tid] : 0;
-    const int QL = tid < num_reqs ? valid_q_len(qsl, tid, num_tokens) : 0;
-    if (tid < num_reqs) {
+    const bool mine = tid < num_reqs;
+    const int L = mine ? seq_lens[tid] : 0;
+    const int QL = mine ? valid_q_len(qsl, tid, num_tokens) : 0;
+    uint32_t part = (mine ? plan_batch_term(tid, qsl[tid + 1], L) : 0u) +
+                    (tid == 0 ? (uint32_t)qsl[0] * 374761393u : 0u);
+    int lmax = max(L, 0);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      part += __shfl_xor(part, off, 64);
+      lmax = max(lmax, __shfl_xor(lmax, off, 64));
+    }
+    if ((tid & 63) == 0) {
+      atomicAdd(&batch_sum, part);
+      atomicMax(&max_len, lmax);
+    }
+    if (mine) {
       sm.len[tid] = L;
       sm.qlen[tid] = QL;
     }
+    int* hist = sm.incl;   // requests per length bucket (the scans below reuse it)
+    int* cursor = sm.aux;  // next free rank of each bucket
+    hist[tid] = 0;
     __syncthreads();
-    if (tid < num_reqs) {
-      int rank = 0;
-      for (int j = 0; j < num_reqs; ++j) {
-        const int Lj = sm.len[j];
-        rank += (Lj > L || (Lj == L && j < tid)) ? 1 : 0;
-      }
-      sm.req[rank] = tid;
+    // Rank by seq_len, longest first, as a bucket sort over 1024 buckets of
+    // the length range (the order within a bucket, and so the list's order,
+    // may vary between calls; no result depends on it).
+    const int top = max(max_len, 1);
+    const int bucket = mine ? (int)((int64_t)(top - min(max(L, 0), top)) * (kPlanReqs - 1) / top)
+                            : 0;
+    if (mine) atomicAdd(&hist[bucket], 1);
+    __syncthreads();
+    {
+      const int h = hist[tid];
+      int tot;
+      const int incl = block_scan_1024(h, sm.wave, &tot);
+      cursor[tid] = incl - h;
     }
+    __syncthreads();
+    if (mine) sm.req[atomicAdd(&cursor[bucket], 1)] = tid;
     __syncthreads();
     // pass 0: prefill tiles, in rank order
     {
@@ -305,13 +329,18 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
       __syncthreads();
       // units with partition index k: decode requests whose split count exceeds k
       int pcarry = 0;
-      for (int kb = 0; kb < max_splits; kb += kPlanReqs) {
-        const int k = kb + tid;
-        const int ck = k < max_splits ? first_not_above(sm.dns, nd, k) : 0;
-        int tot;
-        const int incl = block_scan_1024(ck, sm.wave, &tot);
-        if (k < max_splits) sm.pk[k + 1] = pcarry + incl;
-        pcarry += tot;
+      if (max_splits == 1) {  // one partition each: nothing to count
+        pcarry = nd;
+        if (tid == 0) sm.pk[1] = nd;
+      } else {
+        for (int kb = 0; kb < max_splits; kb += kPlanReqs) {
+          const int k = kb + tid;
+          const int ck = k < max_splits ? first_not_above(sm.dns, nd, k) : 0;
+          int tot;
+          const int incl = block_scan_1024(ck, sm.wave, &tot);
+          if (k < max_splits) sm.pk[k + 1] = pcarry + incl;
+          pcarry += tot;
+        }
       }
       if (tid == 0) sm.pk[0] = 0;
       __syncthreads();
@@ -327,6 +356,14 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
       carry += pcarry;
     }
   } else {
+    {
+      uint32_t part = tid == 0 ? (uint32_t)qsl[0] * 374761393u : 0u;
+      for (int r = tid; r < num_reqs; r += kPlanReqs)
+        part += plan_batch_term(r, qsl[r + 1], seq_lens[r]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      if ((tid & 63) == 0) atomicAdd(&batch_sum, part);
+    }
     for (int pass = 0; pass < 2; ++pass) {
       for (int rb = 0; rb < num_reqs; rb += kPlanReqs) {
         const int r = rb + tid;
