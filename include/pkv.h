@@ -49,12 +49,19 @@
  * - Integer index tensors are int32 except slot_mapping (int64, -1 = no
  *   write).  Block pools are two separate tensors:
  *     K pool: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major)
- *     V pool: [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major)
+ *     V pool: [num_blocks][num_kv_heads][head_dim * block_size], each
+ *             (block, head) run in tiles of 16 dims x 4 tokens:
+ *             element (dim, t) at ((dim / 16) * (block_size / 4) + t / 4) * 64
+ *             + (dim % 16) * 4 + t % 4 (when 16 does not divide head_dim the
+ *             tile spans all dims, when 4 does not divide block_size all
+ *             tokens: then the run is plain [head_dim][block_size])
  *   The pages leave the cache layout to the kernel ("Inside vLLM: Following
  *   One Request from the API to GPU Execution", Part 5, which notes that
- *   different write/read kernel pairs use different layouts).  A dim-major V
- *   block makes the P.V contraction over tokens read 16 consecutive tokens
- *   of one dimension as one contiguous run.
+ *   different write/read kernel pairs use different layouts).  In a V tile
+ *   the 4 tokens of one dimension are one contiguous run, the operand unit
+ *   of the P.V contraction over tokens, and a single token's row of 128
+ *   16-bit values spans 8 cache lines of 128 bytes per head (a dim-major
+ *   run would spread it over 32, each partly written).
  * - Ordering: the KV write of a step must be enqueued before the attention
  *   that reads it, on the same stream or behind an event.  The pages make the
  *   same requirement explicit with a dummy data dependency ("Inside vLLM...",
@@ -217,7 +224,8 @@ pkv_status pkv_prepare_input_ids(const int32_t* token_table, int64_t row_width,
  * is token-granular while reads are block-granular.  For every i with
  * s = slot_mapping[i] in [0, num_blocks * block_size) and every kv head h:
  *   K pool[s / block_size][h][s % block_size][:] = key[i][h][:]
- *   V pool[s / block_size][h][:][s % block_size] = value[i][h][:]
+ *   V pool element (dim, s % block_size) of run (s / block_size, h)
+ *     = value[i][h][dim] for every dim (tiled order above)
  * Bytes are copied unchanged.  Slots < 0 (padding rows) and slots past the
  * pool are skipped.
  *

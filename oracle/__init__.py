@@ -204,7 +204,9 @@ def kv_write(key, value, key_cache, value_cache, slot_mapping, block_size: int) 
 
     ``key``/``value`` are [T, Hkv, d] CPU tensors or arrays (any 2- or 4-byte
     dtype; bytes are copied unchanged).  ``key_cache`` is [nb, Hkv, bs, d],
-    ``value_cache`` is [nb, Hkv, d, bs].
+    ``value_cache`` holds nb * Hkv runs of d * bs elements, each in
+    tiles of 16 dims x 4 tokens ([d / 16][bs / 4][16][4], plain [d][bs] when
+    16 does not divide d or 4 does not divide bs).
     """
     T, H, d = key.shape
     nb = key_cache.shape[0]

@@ -43,7 +43,9 @@
  *
  * Cache layout (an interface fact, not part of the method; the pages leave the
  * layout open): K pool [num_blocks][num_kv_heads][block_size][head_dim],
- * V pool [num_blocks][num_kv_heads][head_dim][block_size], row-major.
+ * row-major; each (block, head) run of the 16-bit and fp32 V pool holds
+ * tiles of 16 dims x 4 tokens, [dim / 16][token / 4][dim % 16][token % 4]
+ * (see orc_v_elem).
  *
  * Readings of points the pages leave open (each also listed in the design
  * notes of the repository):
@@ -219,9 +221,19 @@ static int64_t orc_k_elem(int64_t block, int32_t head, int32_t tok, int32_t dim,
   return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;
 }
 
+/* Element of (block, head, token, dim) in a 16-bit or fp32 V pool.  Each
+ * (block, head) run of head_dim * block_size elements is cut into tiles of
+ * DW dims x TG tokens, ordered [dim / DW][token / TG][dim % DW][token % TG],
+ * with DW = 16 and TG = 4 -- or DW = head_dim when 16 does not divide it,
+ * and TG = block_size when 4 does not divide it (then the run is plain
+ * [dim][token]).  An interface fact of the library's pools. */
 static int64_t orc_v_elem(int64_t block, int32_t head, int32_t tok, int32_t dim,
                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim) {
-  return ((block * num_kv_heads + head) * (int64_t)head_dim + dim) * block_size + tok;
+  const int32_t dw = head_dim % 16 == 0 ? 16 : head_dim;
+  const int32_t tg = block_size % 4 == 0 ? 4 : block_size;
+  const int64_t run = (block * num_kv_heads + head) * (int64_t)head_dim * block_size;
+  const int64_t tile = (int64_t)(dim / dw) * (block_size / tg) + tok / tg;
+  return run + tile * dw * tg + (int64_t)(dim % dw) * tg + tok % tg;
 }
 
 static int cmp_i64(const void* a, const void* b) {

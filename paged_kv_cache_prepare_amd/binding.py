@@ -323,9 +323,10 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                     k_scale: torch.Tensor | None = None,
                     v_scale: torch.Tensor | None = None, planned: bool = False) -> torch.Tensor:
     """pkv_paged_attention_varlen (or _fp8 when k_scale / v_scale are given).
-    q: [T, Hq, d]; 16-bit pools: K [nb, Hkv, 16, d], V [nb, Hkv, d, 16]; FP8
-    pools (uint8): K [nb, Hkv, 16, d], V [nb, Hkv, d * 16]; scales: one-element
-    float32 device tensors.  planned=True: pkv_paged_attention_run over the work
+    q: [T, Hq, d]; 16-bit pools: K [nb, Hkv, 16, d], V [nb, Hkv, d * 16] in
+    tiles of 16 dims x 4 tokens (workloads.value_pool); FP8 pools (uint8):
+    K [nb, Hkv, 16, d], V [nb, Hkv, d * 16]; scales: one-element float32
+    device tensors.  planned=True: pkv_paged_attention_run over the work
     list a paged_attention_plan call left in ``workspace``."""
     T, Hq, d = q.shape
     nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]

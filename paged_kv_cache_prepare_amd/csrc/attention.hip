@@ -28,8 +28,8 @@
 //             lands with 4 tokens of one column per lane, which is exactly
 //             the B-operand layout of P^T in O^T = V^T P^T, so the softmax
 //             probabilities feed the second MFMA without leaving registers.
-//             V blocks are stored dim-major, so V^T rows are contiguous runs
-//             of 4 tokens (8 bytes) per lane.  Online softmax: running max by
+//             V runs are tiles of 16 dims x 4 tokens, so a lane's V^T
+//             operand (4 tokens of one dim) is one contiguous 8-byte run.  Online softmax: running max by
 //             two cross-lane shuffles, per-lane partial sums reduced once.
 //  3. reduce: combines partition partials of split decode items.
 // fp32 path: one wave per (row, q head), fp32 vector math, no partitions.
@@ -415,7 +415,10 @@ struct Geometry {
 };
 
 // Loads of one 32-token step: K rows of blocks j0 and j1 (A operand of S^T),
-// and 4-token V^T runs of both blocks for every 16-dim tile.
+// and 4-token V^T runs of both blocks for every 16-dim tile.  A (block, kv
+// head) V run is [dim / 16][token / 4][dim % 16][token % 4] x 2 bytes: tile dt
+// is 512 contiguous bytes, and the 8 bytes of (dim 16 dt + n, tokens
+// 4g..4g+3) sit at 512 dt + 128 g + 8 n.
 template <int D>
 struct StepLoads {
   bf16x8 k0[Geometry<D>::KS], k1[Geometry<D>::KS];
@@ -583,7 +586,7 @@ __device__ __attribute__((always_inline)) inline void walk_steps(
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int k_lane = (n * D + 8 * g) * 2;
-  const int v_lane = (n * kBlock + 4 * g) * 2;
+  const int v_lane = 128 * g + 8 * n;
   const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
   const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
 
@@ -976,8 +979,9 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, float vs, int
 // over several rows costs extra cycles, measured with the LDS bank-conflict
 // counter).  Every operand read is 16*lane or a lane base plus an immediate:
 //  * K:   [block t][8-dim chunk c][16 tokens] x 16 bytes;
-//  * V^T: [k-step k][16-dim tile][lane group g][16 dims] x 16 bytes, each 16
-//    bytes = tokens 4g..4g+3 of block 2k, then of block 2k+1.
+//  * V^T: per block, the pool's run as it is (tiles of 16 dims x 4 tokens);
+//    a lane's operand (8 tokens of one dim) is two 8-byte reads 128 bytes
+//    apart, and lane groups 2k, 2k+1 read 256 contiguous bytes each time.
 // The staging loads pick, per lane, the global 16-byte chunk whose LDS slot
 // makes each 16-lane write group fill one 256-byte segment as well.
 // The softmax denominator is accumulated by one more MFMA per PV k-step, with
@@ -1006,16 +1010,13 @@ struct PrefillSmem {
   alignas(4) unsigned char valid[2][4];  // per buffer: block b of the step is readable
 };
 
-// Zero element e of an 8 x bf16 run when first + e >= limit.
-__device__ inline u32x4 keep_below(u32x4 v, int first, int limit) {
-  unsigned m[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const unsigned lo = (first + 2 * i < limit) ? 0x0000FFFFu : 0u;
-    const unsigned hi = (first + 2 * i + 1 < limit) ? 0xFFFF0000u : 0u;
-    m[i] = lo | hi;
-  }
-  return u32x4{v.x & m[0], v.y & m[1], v.z & m[2], v.w & m[3]};
+// Zero element e of a (2 dims x 4 tokens) bf16 unit when first + e % 4 >= limit.
+__device__ inline u32x4 keep_below4(u32x4 v, int first, int limit) {
+  const unsigned lo = (first < limit) ? 0x0000FFFFu : 0u;
+  const unsigned m0 = lo | ((first + 1 < limit) ? 0xFFFF0000u : 0u);
+  const unsigned m1 = ((first + 2 < limit) ? 0x0000FFFFu : 0u) |
+                      ((first + 3 < limit) ? 0xFFFF0000u : 0u);
+  return u32x4{v.x & m0, v.y & m1, v.z & m0, v.w & m1};
 }
 
 template <typename T>
@@ -1143,8 +1144,11 @@ template <int D>
 __device__ __attribute__((always_inline)) inline void prefill_v_read(
     bf16x8 (&vf)[Geometry<D>::DT], const char* vb, int h) {
 #pragma unroll
-  for (int dt = 0; dt < Geometry<D>::DT; ++dt)
-    vf[dt] = lds_ld<bf16x8>(vb, 2 * h * PrefillLayout<D>::vRun + dt * 512);
+  for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
+    const u32x2 lo = lds_ld<u32x2>(vb, 2 * h * PrefillLayout<D>::vRun + dt * 512);
+    const u32x2 hi = lds_ld<u32x2>(vb, 2 * h * PrefillLayout<D>::vRun + dt * 512 + 128);
+    vf[dt] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+  }
 }
 // O^T += V^T P^T over keys 32h..32h+31, and the denominators (an all-ones A
 // operand sums exactly the bf16 weights the numerator uses).
@@ -1262,14 +1266,15 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
   // 16i..16i+15 of its 1 KB destination).
   //   K run: 1 KB per k-step s; lane (m = i & 15, gg = i >> 4) holds dims
   //          8(4s + gg)..+7 of token m, the MFMA A-operand order.
-  //   V run: chunk (dim, c) = tokens 8c..8c+7 of one dim, at 16-byte slot
-  //          (dim / 16) * 32 + c * 16 + dim % 16, so the 4-token runs that
-  //          form a PV operand are read 8 bytes per lane, conflict-free.
+  //   V run: the pool run verbatim: 16-byte slot 32 dt + 8 u + p holds
+  //          dims 16 dt + 2p and +1 of tokens 4u..4u+3.  A PV operand (8
+  //          tokens of one dim) is two 8-byte reads of token groups 2c and
+  //          2c+1, 128 bytes apart.
   // Source offsets of copy q: K token (lane & 15), dims 8(4q + (lane >> 4));
   // V slot q * 64 + lane.  Both are a lane base plus q times a constant.
   const int k_src = (lane & 15) * 2 * D + 16 * (lane >> 4);            // + 64 q
-  const int v_src = ((lane >> 5) * 16 + (lane & 15)) * 2 * kBlock +     // + 1024 q
-                    16 * ((lane >> 4) & 1);
+  const int v_u = (lane >> 3) & 3;  // token group of this lane's V slots
+  const int v_src = 16 * lane;      // + 1024 q
   typedef __attribute__((address_space(3))) void lds_void;
   // Issue this wave's copy of block `wave` of a step into LDS buffer `buf`.
   // Returns whether the block is readable (inside the context, id inside the
@@ -1329,24 +1334,33 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
       const int tok0 = step * kPrefillStep + wave * kBlock;
 #pragma unroll
       for (int q = 0; q < KQ; ++q) {
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (!ok) break;
+        // K: token lane & 15, dims 8(4q + (lane >> 4)) .. + 7
+        const u32x2 k8 = *reinterpret_cast<const u32x2*>(
+            stage_k + (lane & 15) * D + 8 * (4 * q + (lane >> 4)));
+        *reinterpret_cast<u32x4*>(kdst + q * 1024 + 16 * lane) =
+            __builtin_bit_cast(u32x4, fp8x8_to_bf16(k8.x, k8.y));
+      }
+      // V: lane (m, u, p) = (lane >> 5, (lane >> 3) & 3, lane & 7) reads the
+      // 32 staged bytes of token group u and dims 64 m + 2p + {0, 1} + 16 k
+      // (k = 0..3) -- word k of each 16-byte half holds 4 tokens of one of
+      // them -- and writes bf16 slots 32 (4m + k) + 8u + p, so each 16-lane
+      // group stores 256 contiguous bytes.
+      if (lane < D / 2) {
+        const int m = lane >> 5, u = (lane >> 3) & 3, p = lane & 7;
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
         if (ok) {
-          // K: token lane & 15, dims 8(4q + (lane >> 4)) .. + 7
-          const u32x2 k8 = *reinterpret_cast<const u32x2*>(
-              stage_k + (lane & 15) * D + 8 * (4 * q + (lane >> 4)));
-          kv = __builtin_bit_cast(u32x4, fp8x8_to_bf16(k8.x, k8.y));
-          // V slot S: dim 16(S / 32) + S % 16, tokens 8c .. 8c+7 with c = (S / 16) % 2,
-          // held as token groups 2c and 2c+1 of the FP8 run
-          const int S = q * 64 + lane;
-          const int dim = 16 * (S >> 5) + (S & 15), c = (S >> 4) & 1;
-          const int base = ((dim >> 6) * 4 + 2 * c) * 256 + (dim & 15) * 16 + ((dim >> 4) & 3) * 4;
-          const unsigned w0 = *reinterpret_cast<const unsigned*>(stage_v + base);
-          const unsigned w1 = *reinterpret_cast<const unsigned*>(stage_v + base + 256);
-          vv = __builtin_bit_cast(u32x4, fp8x8_to_bf16(w0, w1));
-          if (tok0 + kBlock > L) vv = keep_below(vv, tok0 + 8 * c, L);
+          lo = *reinterpret_cast<const u32x4*>(stage_v + (m * 4 + u) * 256 + p * 32);
+          hi = *reinterpret_cast<const u32x4*>(stage_v + (m * 4 + u) * 256 + p * 32 + 16);
         }
-        if (ok) *reinterpret_cast<u32x4*>(kdst + q * 1024 + 16 * lane) = kv;
-        *reinterpret_cast<u32x4*>(vdst + q * 1024 + 16 * lane) = vv;
+        const bool tail = ok && tok0 + kBlock > L;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          u32x4 vv = {0u, 0u, 0u, 0u};
+          if (ok) vv = __builtin_bit_cast(u32x4, fp8x8_to_bf16(lo[k], hi[k]));
+          if (tail) vv = keep_below4(vv, tok0 + 4 * u, L);
+          *reinterpret_cast<u32x4*>(vdst + (32 * (4 * m + k) + 8 * u + p) * 16) = vv;
+        }
       }
       return;
     }
@@ -1361,7 +1375,7 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
 #pragma unroll
       for (int q = 0; q < KQ; ++q) {
         u32x4* pv = reinterpret_cast<u32x4*>(vdst + q * 1024 + 16 * lane);
-        *pv = keep_below(*pv, tok0 + 8 * (((q * 64 + lane) >> 4) & 1), L);
+        *pv = keep_below4(*pv, tok0 + 4 * v_u, L);
       }
     }
   };
@@ -1372,9 +1386,10 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
   // K operand row n of tile 0 is key 8(n / 4) + n % 4 of the half: block
   // n / 8 of the half, token 8((n / 4) % 2) + n % 4; lane (n, g) reads dims
   // 8(4k + g)..+7 of it.  V operand lane (n, g) reads dim 16 dt + n, keys
-  // 8(g % 2)..+7 of block g / 2 of the half.
+  // 8(g % 2)..+7 of block g / 2 of the half: token groups 2(g % 2) (at
+  // 256 (g % 2) in each tile) and 2(g % 2) + 1 (128 bytes further).
   const int k_rd = (n >> 3) * Lay::kRun + (g * 16 + 8 * ((n >> 2) & 1) + (n & 3)) * 16;
-  const int v_rd = (g >> 1) * Lay::vRun + ((g & 1) * 16 + n) * 16;
+  const int v_rd = (g >> 1) * Lay::vRun + (g & 1) * 256 + n * 8;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
                                                        0x3F803F80u});
 
@@ -1534,6 +1549,12 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a, int32_t gr
 // fp32 path: one wave per (row, q head)
 // ---------------------------------------------------------------------------
 
+// Element of (dim, token) in a (block, kv head) V run: tiles of 16 dims x 4
+// tokens, [dim / 16][token / 4][dim % 16][token % 4].
+__device__ inline int v_tile_elem(int dim, int tok) {
+  return ((dim >> 4) * (kBlock / 4) + (tok >> 2)) * 64 + (dim & 15) * 4 + (tok & 3);
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int32_t group) {
   constexpr int PER = D / 64;
@@ -1588,7 +1609,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int32_t group)
     l = l * alpha + pj;
 #pragma unroll
     for (int k = 0; k < PER; ++k)
-      o[k] = o[k] * alpha + pj * vc[(head_base * D + lane + 64 * k) * kBlock + off];
+      o[k] = o[k] * alpha + pj * vc[head_base * D * kBlock + v_tile_elem(lane + 64 * k, off)];
     m = m_new;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -7,12 +7,13 @@
 // One workgroup handles 16 consecutive tokens of one kv head.
 //  * K pool rows [block][head][offset][:] are contiguous per token, so each
 //    thread moves one 16-byte chunk (global load -> global store).
-//  * V pool blocks are dim-major ([block][head][dim][offset]).  The 16 rows
-//    are staged in LDS, then each thread writes one dimension for a run of
-//    16 / element-size consecutive tokens: when those tokens occupy
-//    consecutive offsets of one block (a prompt chunk) the run is a single
-//    16-byte store and a whole block row is written by adjacent threads;
-//    otherwise (scattered decode tokens) it falls back to element stores.
+//  * V runs ([block][head] runs of head_dim x 16) are tiles of 16 dims x 4
+//    offsets (v_elem), so that a decode token's row touches 8 cache lines
+//    per head (head_dim 128) rather than 32: each partly written line costs
+//    the next kernel HBM time when it is written back.  The 16 rows are
+//    staged in LDS, then each thread writes one 16-byte unit (16 / (4 E)
+//    dims x 4 offsets): one store when its 4 tokens fill aligned consecutive
+//    offsets of one block (a prompt chunk), element stores otherwise.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -23,6 +24,19 @@ constexpr int kTileTokens = 16;
 constexpr int kMaxRowBytes = 1024;  // head_dim * element bytes
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Element of (dim, offset) inside one (block, head) V run of head_dim x
+// block_size elements: tiles of DW dims x TG offsets ordered
+// [dim / DW][offset / TG][dim % DW][offset % TG], DW = 16 and TG = 4 (DW =
+// head_dim when 16 does not divide it, TG = block_size when 4 does not).  A
+// decode token's row then lands in head_dim / 16 cache lines per head
+// instead of one line per 4 dims.
+__device__ inline int64_t v_elem(int dim, int off, int head_dim, int block_size) {
+  const int dw = head_dim % 16 == 0 ? 16 : head_dim;
+  const int tg = block_size % 4 == 0 ? 4 : block_size;
+  return ((int64_t)(dim / dw) * (block_size / tg) + off / tg) * (dw * tg) + (dim % dw) * tg +
+         off % tg;
+}
 
 template <int E>  // element bytes: 2 (bf16) or 4 (fp32)
 __global__ __launch_bounds__(kThreads) void kv_write_kernel(
@@ -71,43 +85,59 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
   }
   __syncthreads();
 
+  // V runs are tiles of 16 dims x 4 offsets (v_elem).  A 16-byte unit of a
+  // tile is 16 / (4 E) dims x 4 offsets; it is one store when its 4 tokens
+  // are this tile's consecutive slots starting at an offset divisible by 4
+  // (a prompt chunk), element stores otherwise (scattered decode tokens).
   const elem_t* s_elems = reinterpret_cast<const elem_t*>(s_v);
-  const int row_elems = head_dim;  // elements of one staged row
-  constexpr int kGroups = kTileTokens / kVecElems;
-  for (int w = tid; w < head_dim * kGroups; w += kThreads) {
-    const int dim = w / kGroups;
-    const int gi = w - dim * kGroups;
-    const int tk0 = gi * kVecElems;
-    const int64_t s0 = s_slot[tk0];
-    bool run = s0 >= 0;
-    elem_t vals[kVecElems];
+  const int64_t run = (int64_t)head_dim * block_size;  // elements of one (block, head) run
+  if (head_dim % 16 == 0 && block_size % 4 == 0) {
+    constexpr int kDims = 4 / E;               // dims per 16-byte unit
+    constexpr int kUnits = 16 / kDims;         // units per tile and token group
+    const int units = (head_dim / 16) * 4 * kUnits;
+    for (int w = tid; w < units; w += kThreads) {
+      const int dim0 = (w / (4 * kUnits)) * 16 + (w % kUnits) * kDims;
+      const int tk0 = 4 * ((w / kUnits) & 3);
+      const int64_t s0 = s_slot[tk0];
+      bool whole = s0 >= 0 && (s0 & 3) == 0;
+      elem_t vals[4 * kDims];  // [dim][token]
 #pragma unroll
-    for (int j = 0; j < kVecElems; ++j) {
-      vals[j] = s_elems[(tk0 + j) * row_elems + dim];
-      run = run && s_slot[tk0 + j] == s0 + j;
-    }
-    if (run) {
-      const int64_t blk = s0 / block_size;
-      const int64_t off = s0 - blk * block_size;
-      char* dst = value_cache + (((blk * num_kv_heads + h) * head_dim + dim) * block_size + off) * E;
-      run = off + kVecElems <= block_size && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
-      if (run) {
+      for (int j = 0; j < 4; ++j) {
+        whole = whole && s_slot[tk0 + j] == s0 + j;
+#pragma unroll
+        for (int c = 0; c < kDims; ++c) vals[c * 4 + j] = s_elems[(tk0 + j) * head_dim + dim0 + c];
+      }
+      if (whole) {
+        const int64_t blk = s0 / block_size;
+        const int off = (int)(s0 - blk * block_size);
         u32x4 packed;
         __builtin_memcpy(&packed, vals, 16);
-        *reinterpret_cast<u32x4*>(dst) = packed;
+        *reinterpret_cast<u32x4*>(
+            value_cache + ((blk * num_kv_heads + h) * run + v_elem(dim0, off, head_dim, block_size)) * E) =
+            packed;
+        continue;
       }
-    }
-    if (!run) {
 #pragma unroll
-      for (int j = 0; j < kVecElems; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const int64_t s = s_slot[tk0 + j];
         if (s < 0) continue;
         const int64_t blk = s / block_size;
-        const int64_t off = s - blk * block_size;
-        *reinterpret_cast<elem_t*>(
-            value_cache + (((blk * num_kv_heads + h) * head_dim + dim) * block_size + off) * E) =
-            vals[j];
+        const int off = (int)(s - blk * block_size);
+        elem_t* dst = reinterpret_cast<elem_t*>(value_cache) + (blk * num_kv_heads + h) * run;
+#pragma unroll
+        for (int c = 0; c < kDims; ++c) dst[v_elem(dim0 + c, off, head_dim, block_size)] = vals[c * 4 + j];
       }
+    }
+  } else {  // untiled run ([dim][offset]): element stores
+    for (int w = tid; w < kTileTokens * head_dim; w += kThreads) {
+      const int tk = w / head_dim, dim = w - tk * head_dim;
+      const int64_t s = s_slot[tk];
+      if (s < 0) continue;
+      const int64_t blk = s / block_size;
+      const int off = (int)(s - blk * block_size);
+      reinterpret_cast<elem_t*>(value_cache)[(blk * num_kv_heads + h) * run +
+                                              v_elem(dim, off, head_dim, block_size)] =
+          s_elems[tk * head_dim + dim];
     }
   }
 }

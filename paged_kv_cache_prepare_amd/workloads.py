@@ -67,7 +67,7 @@ class Workload:
     key: torch.Tensor = None           # [T, Hkv, d]
     value: torch.Tensor = None         # [T, Hkv, d]
     key_cache: torch.Tensor = None     # [nb, Hkv, bs, d]
-    value_cache: torch.Tensor = None   # [nb, Hkv, d, bs]
+    value_cache: torch.Tensor = None   # [nb, Hkv, d * bs] (value_pool order), or FP8 codes
     notes: dict = field(default_factory=dict)
     kv_scales: tuple = None            # (k_scale, v_scale) when the pools hold FP8 codes
 
@@ -185,6 +185,7 @@ def build(name: str, nst, nct, *, num_q_heads: int, num_kv_heads: int, head_dim:
     hist = torch.from_numpy(history).to(device)
     kc.masked_fill_(~hist[:, None, :, None], float("nan"))
     vc.masked_fill_(~hist[:, None, None, :], float("nan"))
+    vc = value_pool(vc)
     q = _randn(gen, (T, H, d), dtype, device)
     k_new = _randn(gen, (T, Hkv, d), dtype, device)
     v_new = _randn(gen, (T, Hkv, d), dtype, device)
@@ -197,6 +198,30 @@ def build(name: str, nst, nct, *, num_q_heads: int, num_kv_heads: int, head_dim:
     wl.notes["shared_blocks"] = n_shared_blocks
     wl.notes["unique_blocks"] = unique_need
     return wl
+
+
+def _value_tiles(head_dim: int, block_size: int) -> tuple[int, int]:
+    return (16 if head_dim % 16 == 0 else head_dim), (4 if block_size % 4 == 0 else block_size)
+
+
+def value_pool(logical: torch.Tensor) -> torch.Tensor:
+    """A 16-bit or fp32 V pool from its logical form [nb, Hkv, d, bs] (element
+    [b, h, dim, tok]): [nb, Hkv, d * bs], each (block, head) run in tiles of
+    16 dims x 4 tokens, [dim / 16][tok / 4][dim % 16][tok % 4] (one tile
+    spans all dims when 16 does not divide d, all tokens when 4 does not
+    divide bs)."""
+    nb, H, d, bs = logical.shape
+    dw, tg = _value_tiles(d, bs)
+    x = logical.reshape(nb, H, d // dw, dw, bs // tg, tg).transpose(3, 4)
+    return x.reshape(nb, H, d * bs).contiguous()
+
+
+def value_logical(pool: torch.Tensor, head_dim: int, block_size: int) -> torch.Tensor:
+    """The inverse of value_pool: [nb, Hkv, d, bs] from a V pool."""
+    nb, H = pool.shape[0], pool.shape[1]
+    dw, tg = _value_tiles(head_dim, block_size)
+    x = pool.reshape(nb, H, head_dim // dw, block_size // tg, dw, tg).transpose(3, 4)
+    return x.reshape(nb, H, head_dim, block_size).contiguous()
 
 
 def fp8_value_order(head_dim: int, block_size: int = BLOCK_SIZE) -> np.ndarray:
@@ -223,7 +248,8 @@ def to_fp8(wl: Workload, k_scale: float, v_scale: float) -> Workload:
 
     kc = codes(wl.key_cache, k_scale).contiguous()
     order = torch.from_numpy(fp8_value_order(d, bs)).to(wl.value_cache.device)
-    vc = codes(wl.value_cache, v_scale).reshape(nb, H, d * bs)[:, :, order].contiguous()
+    logical_v = value_logical(wl.value_cache, d, bs)
+    vc = codes(logical_v, v_scale).reshape(nb, H, d * bs)[:, :, order].contiguous()
     out = Workload(**{f: getattr(wl, f) for f in wl.__dataclass_fields__})
     out.name = wl.name + "-fp8"
     out.key_cache, out.value_cache = kc, vc

@@ -33,8 +33,12 @@ MUTANTS = {
     "softmax sign flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     "gqa interleaved heads": ("for (int32_t h = g * group; h < (g + 1) * group; ++h) {",
                               "for (int32_t h = g; h < num_q_heads; h += num_kv_heads) {"),
-    "value layout transposed": ("return ((block * num_kv_heads + head) * (int64_t)head_dim + dim) * block_size + tok;",
-                                "return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;"),
+    "value tiles in token-major order": (
+        "const int64_t tile = (int64_t)(dim / dw) * (block_size / tg) + tok / tg;",
+        "const int64_t tile = (int64_t)(tok / tg) * (head_dim / dw) + dim / dw;"),
+    "value tile transposed inside": (
+        "return run + tile * dw * tg + (int64_t)(dim % dw) * tg + tok % tg;",
+        "return run + tile * dw * tg + (int64_t)(tok % tg) * dw + dim % dw;"),
     "gather offset uses block index": ("const int32_t off = j % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          if (kv_dtype",
                                        "const int32_t off = (j / block_size) % block_size;\n        for (int32_t c = 0; c < head_dim; ++c) {\n          if (kv_dtype"),
     "kv write uses key layout for values": (

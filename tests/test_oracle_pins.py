@@ -22,6 +22,38 @@ import torch.nn.functional as F
 
 import oracle
 
+
+def _v_tiles(d, bs):
+    return (16 if d % 16 == 0 else d), (4 if bs % 4 == 0 else bs)
+
+
+def v_elem(d, bs, dim, tok):
+    """Element of (dim, tok) inside one (block, head) V run: tiles of 16 dims x
+    4 tokens, [dim / 16][tok / 4][dim % 16][tok % 4] (one tile spans every dim
+    when 16 does not divide d, every token when 4 does not divide bs)."""
+    dw, tg = _v_tiles(d, bs)
+    return ((dim // dw) * (bs // tg) + tok // tg) * dw * tg + (dim % dw) * tg + tok % tg
+
+
+def v_pool(logical):
+    """A V pool [nb, Hkv, d * bs] from its logical form [nb, Hkv, d, bs]."""
+    nb, H, d, bs = logical.shape
+    out = torch.empty(nb, H, d * bs, dtype=logical.dtype)
+    for dim in range(d):
+        for tok in range(bs):
+            out[:, :, v_elem(d, bs, dim, tok)] = logical[:, :, dim, tok]
+    return out
+
+
+def v_logical(pool, d, bs):
+    """The logical [nb, Hkv, d, bs] view of a V pool (a copy)."""
+    flat = pool.reshape(pool.shape[0], pool.shape[1], d * bs)
+    out = torch.empty(pool.shape[0], pool.shape[1], d, bs, dtype=pool.dtype)
+    for dim in range(d):
+        for tok in range(bs):
+            out[:, :, dim, tok] = flat[:, :, v_elem(d, bs, dim, tok)]
+    return out
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "prepare_page_examples.json")
 
 
@@ -201,17 +233,18 @@ def test_prepare_empty_batch():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_kv_write_post_state(dtype):
+@pytest.mark.parametrize("nb,H,bs,d,T", [(7, 3, 4, 8, 9), (5, 2, 8, 32, 11)])
+def test_kv_write_post_state(dtype, nb, H, bs, d, T):
     g = torch.Generator().manual_seed(3)
-    nb, H, bs, d, T = 7, 3, 4, 8, 9
     kc = torch.randn(nb, H, bs, d, generator=g).to(dtype)
-    vc = torch.randn(nb, H, d, bs, generator=g).to(dtype)
+    vc = v_pool(torch.randn(nb, H, d, bs, generator=g).to(dtype))
     key = torch.randn(T, H, d, generator=g).to(dtype)
     val = torch.randn(T, H, d, generator=g).to(dtype)
     slots = torch.randperm(nb * bs, generator=g)[:T].numpy().astype(np.int64)
     slots[4] = -1  # padding row: no write
     kc0, vc0 = kc.clone(), vc.clone()
     oracle.kv_write(key, val, kc, vc, slots, block_size=bs)
+    vc, vc0 = v_logical(vc, d, bs), v_logical(vc0, d, bs)
     written = np.zeros((nb, bs), bool)
     for i, s in enumerate(slots):
         if s < 0:
@@ -225,6 +258,36 @@ def test_kv_write_post_state(dtype):
                        kc0[keep[:, None, :, None].expand_as(kc0)])
     assert torch.equal(vc[keep[:, None, None, :].expand_as(vc)],
                        vc0[keep[:, None, None, :].expand_as(vc0)])
+
+
+def test_value_layout_positions():
+    """Where one token's V row lands in the pool, element by element, for a
+    tiled run (head_dim 32, block_size 8) and an untiled one (head_dim 8,
+    block_size 6): the documented order written out, not v_elem."""
+    for d, bs, slot, expect in (
+            (32, 8, 2 * 8 + 5, lambda dim: ((dim // 16) * 2 + 1) * 64 + (dim % 16) * 4 + 1),
+            (8, 6, 1 * 6 + 4, lambda dim: dim * 6 + 4)):
+        H = 2
+        kc = torch.zeros(4, H, bs, d)
+        vc = torch.zeros(4, H, d * bs)
+        val = (torch.arange(H * d, dtype=torch.float32) + 1).reshape(1, H, d)
+        oracle.kv_write(val, val, kc, vc, [slot], block_size=bs)
+        blk = slot // bs
+        for h in range(H):
+            for dim in range(d):
+                assert vc[blk, h, expect(dim)] == h * d + dim + 1, (d, bs, h, dim)
+        assert int((vc != 0).sum()) == H * d
+
+
+def test_value_layout_decode_row_lines():
+    """A 16-bit decode row of head_dim 128 in a 16-token block lands in 8
+    aligned 128-byte lines per head (16 dims x 4 tokens x 2 bytes each), the
+    reason for the tiled V order: a partly written line costs a later
+    write-back."""
+    d, bs = 128, 16
+    for tok in range(bs):
+        lines = {v_elem(d, bs, dim, tok) * 2 // 128 for dim in range(d)}
+        assert len(lines) == 8
 
 
 def test_kv_write_rejects_duplicates_and_range():
@@ -270,6 +333,7 @@ def make_paged(nst, nct, Hq, Hkv, d, bs, seed, dtype=torch.float32, slack=3):
             b, o = int(bt[r, j // bs]), j % bs
             kc[b, :, o, :] = Ks[r][j]
             vc[b, :, :, o] = Vs[r][j]
+    vc = v_pool(vc)
     q = torch.cat([Qs[r][int(nct[r]):] for r in range(R)]).contiguous()
     qsl = np.concatenate([[0], np.cumsum(nst)]).astype(np.int32)
     return dict(Ks=Ks, Vs=Vs, Qs=Qs, nst=nst, nct=nct), dict(
@@ -441,13 +505,14 @@ def test_prepare_write_attention_chain_equals_unpaged_sdpa():
     logical, paged = make_paged(nst, nct, 4, 2, 16, 4, seed=16)
     R = len(nst)
     # wipe this step's slots, then let prepare + kv_write put them back
-    kc, vc = paged["kc"].clone(), paged["vc"].clone()
+    kc, vc = paged["kc"].clone(), v_logical(paged["vc"], 16, 4)
     key = torch.cat([logical["Ks"][r][nct[r]:] for r in range(R)]).contiguous()
     val = torch.cat([logical["Vs"][r][nct[r]:] for r in range(R)]).contiguous()
     prep = oracle.prepare(nst, nct, paged["bt"], block_size=4, num_blocks=kc.shape[0])
     for s in prep["slot_mapping"]:
         kc[s // 4, :, s % 4, :] = float("nan")
         vc[s // 4, :, :, s % 4] = float("nan")
+    vc = v_pool(vc)
     oracle.kv_write(key, val, kc, vc, prep["slot_mapping"], block_size=4)
     out = oracle.attention(paged["q"], kc, vc, prep["query_start_loc"], prep["seq_lens"],
                            paged["bt"], 4, 0.25)
