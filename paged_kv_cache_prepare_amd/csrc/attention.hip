@@ -13,8 +13,9 @@
 //             in the workspace: prefill tiles first, then decode partitions,
 //             longest contexts first.  Host code never reads device data, so
 //             the list is built on the device.
-//  2. main:   one workgroup (4 waves) per work item; prompt-chunk tiles and
-//             single-token decodes of the same step run in this one launch.
+//  2. main:   workgroups of 4 waves; prompt-chunk tiles and single-token
+//             decodes of the same step run in this one launch (prefill
+//             tiles on resident workgroups, one workgroup per decode item).
 //             * decode item = (request, kv head, partition): the q heads of
 //               the kv head (and, for short multi-token queries, their rows)
 //               form the 16-wide N side of v_mfma_f32_16x16x32_bf16; the 4
