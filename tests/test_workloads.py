@@ -68,3 +68,21 @@ def test_config_structure_geometry_matches_the_configs():
         name = workloads.CONFIG_NAMES[idx]
         assert f"Hq {s['num_q_heads']} / Hkv {s['num_kv_heads']}, d {s['head_dim']}" in name
         assert s["dtype"] == torch.bfloat16 and "bf16" in name
+
+
+def test_value_pool_order_and_inverse():
+    """value_pool puts logical element (dim, tok) of a (block, head) run at
+    ((dim // 16) * (bs // 4) + tok // 4) * 64 + (dim % 16) * 4 + tok % 4 (plain
+    [dim][tok] when 16 does not divide d or 4 does not divide bs), and
+    value_logical undoes it."""
+    for d, bs in ((128, 16), (64, 16), (32, 8), (8, 4), (16, 6)):
+        logical = torch.arange(3 * 2 * d * bs, dtype=torch.float32).reshape(3, 2, d, bs)
+        pool = workloads.value_pool(logical)
+        assert pool.shape == (3, 2, d * bs)
+        tiled = d % 16 == 0 and bs % 4 == 0
+        for dim in (0, 1, d // 2, d - 1):
+            for tok in (0, 3, bs - 1):
+                e = (((dim // 16) * (bs // 4) + tok // 4) * 64 + (dim % 16) * 4 + tok % 4
+                     if tiled else dim * bs + tok)
+                assert torch.equal(pool[:, :, e], logical[:, :, dim, tok]), (d, bs, dim, tok)
+        assert torch.equal(workloads.value_logical(pool, d, bs), logical)
