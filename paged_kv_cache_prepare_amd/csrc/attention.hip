@@ -1487,25 +1487,29 @@ union MainSmem {
 // wave's softmax VALU work overlaps the other's MFMAs, and a decode item's
 // start-up latency overlaps the other workgroup's loads.
 //
-// Prefill items (the head of the list) run on P = min(prefill items, two
-// per CU) resident workgroups, each walking its share of the list; decode
-// items are one workgroup each, dispatched after them.  On the 5000-token
-// chunk the resident form is about 4 % faster than one workgroup per tile;
-// for decode items it was slower (a whole-list resident form with a claim
-// counter or a fixed share lost 13-17 % on decode batches), so they keep the
-// hardware dispatcher's balancing.
+// Prefill items (the head of the list) run on P resident workgroups, each
+// walking its share of the list; decode items are one workgroup each,
+// dispatched after them.  P = min(prefill items, `slots`) (two per CU) when
+// the batch is all prompt tiles, and min(prefill items, `slots_mixed`) (one
+// per CU) when decode items follow: each CU then runs one MFMA-bound prompt
+// tile beside HBM-bound decode items instead of finishing the prompt before
+// the decodes start.  On the 5000-token chunk the resident form is about 4 %
+// faster than one workgroup per tile; for decode items it was slower (a
+// whole-list resident form with a claim counter or a fixed share lost
+// 13-17 % on decode batches), so they keep the hardware dispatcher's
+// balancing.
 template <int D, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_main_kernel(
     AttnArgs a, int32_t group, float c2, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items, int32_t max_splits, float* __restrict__ ml,
-    float* __restrict__ opart, int32_t slots) {
+    float* __restrict__ opart, int32_t slots, int32_t slots_mixed) {
   __shared__ MainSmem<D> sm;
   const int n = n_items[0];
   const int n_pre = n_items[kPrefillItemsWord];
   // FP8 pools: k_scale joins the softmax scale, v_scale the output
   const float c2k = KV8 ? c2 * *a.k_scale : c2;
   const float vs = KV8 ? *a.v_scale : 1.f;
-  const int P = min(n_pre, slots);
+  const int P = min(n_pre, n > n_pre ? slots_mixed : slots);
   const int b = blockIdx.x;
   if (b < P) {
     // prefill items: the first P workgroups stay resident and take items
@@ -1686,7 +1690,7 @@ hipError_t launch_run_d(const AttnArgs& a, const AttnPlan& plan, void* workspace
   if (plan.max_items > 0) {
     hipLaunchKernelGGL((attn_main_kernel<D, KV8>), dim3((unsigned)plan.max_items), dim3(kThreads), 0,
                        stream, a, plan.group, c2, items, n_items, plan.max_splits, ml, opart,
-                       2 * device_cu_count());
+                       2 * device_cu_count(), device_cu_count());
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
