@@ -228,8 +228,9 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
     }
     const int64_t blk = s / kTileTokens;
     const int64_t off = s - blk * kTileTokens;
-    *reinterpret_cast<u32x4*>(key_cache + (blk * num_kv_heads + h) * run + off * head_dim +
-                              16 * c) = u32x4{kw[0], kw[1], kw[2], kw[3]};
+    __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]},
+                                reinterpret_cast<u32x4*>(key_cache + (blk * num_kv_heads + h) * run +
+                                                         off * head_dim + 16 * c));
     *reinterpret_cast<u32x4*>(&s_v[tk][16 * c]) = u32x4{vw[0], vw[1], vw[2], vw[3]};
   }
   __syncthreads();
@@ -255,8 +256,8 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
       const int g = (int)(s0 - blk * kTileTokens) / 4;
       u32x4 v;
       __builtin_memcpy(&v, b, 16);
-      *reinterpret_cast<u32x4*>(value_cache + (blk * num_kv_heads + h) * run +
-                                (((int64_t)dq * 4 + g) * 16 + n) * 16) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(value_cache + (blk * num_kv_heads + h) * run +
+                                                              (((int64_t)dq * 4 + g) * 16 + n) * 16));
       continue;
     }
 #pragma unroll
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
       uint8_t* unit = value_cache + (blk * num_kv_heads + h) * run +
                       (((int64_t)dq * 4 + off / 4) * 16 + n) * 16 + off % 4;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) unit[4 * dt] = b[4 * dt + tt];
+      for (int dt = 0; dt < 4; ++dt) __builtin_nontemporal_store(b[4 * dt + tt], &unit[4 * dt]);
     }
   }
 }
