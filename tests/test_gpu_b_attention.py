@@ -53,6 +53,23 @@ def test_attention_config(idx):
     assert_attention_close(got, ref, wl.dtype, f"config {idx} ({'all' if rows is None else len(rows)} rows)")
 
 
+@pytest.mark.parametrize("idx,rows", [(4, "prefill"), (5, "prefill"), (4, "decode")])
+def test_attention_config_rows(idx, rows):
+    """The prompt rows alone (1256 and 1024 tiles: the resident prefill
+    workgroups walk several rounds of the tile list, two per CU) and the
+    decode rows alone, as the benchmark's --rows runs time them."""
+    wl = workloads.config(idx, device=device())
+    group = wl.num_q_heads // wl.num_kv_heads
+    short = wl.num_scheduled_tokens * group <= 16
+    wl = workloads.select(wl, np.nonzero(short if rows == "decode" else ~short)[0])
+    log(f"config {idx} {rows} rows: {wl.num_reqs} requests, {wl.num_tokens} tokens")
+    prep, kc, vc, out = gpu_step(wl)
+    sel = sample_rows(wl)
+    _, _, _, ref = oracle_step(wl, rows=sel)
+    got = out if sel is None else out[torch.from_numpy(sel).long().to(out.device)]
+    assert_attention_close(got, ref, wl.dtype, f"config {idx} {rows} rows")
+
+
 # (nst, nct, Hq, Hkv, d) -- decode items, multi-row decode items (q_len * G <= 16),
 # prefill tiles with ragged tails, chunks that start mid-sequence, empty requests.
 SMALL = [
