@@ -90,3 +90,17 @@ def test_fp8_scale_is_applied_to_keys_and_values():
                             prep["seq_lens"].cpu(), wl.block_table, 16, wl.scale,
                             kv_scales=(0.03, 0.02))
     assert_attention_close(out3, ref3, wl.dtype, "k_scale 0.03")
+
+
+def test_fp8_attention_prompt_rows():
+    """Configuration 4's prompt rows alone over FP8 pools (1256 tiles on the
+    two-per-CU resident prefill workgroups), sampled rows."""
+    wl = workloads.config(4, device=device())
+    group = wl.num_q_heads // wl.num_kv_heads
+    wl = workloads.select(wl, np.nonzero(wl.num_scheduled_tokens * group > 16)[0])
+    wl = workloads.to_fp8(wl, *SCALES)
+    prep, kc, vc, out = gpu_step(wl)
+    rows = sample_rows(wl)
+    _, _, _, ref = oracle_step(wl, rows=rows)
+    got = out if rows is None else out[torch.from_numpy(rows).long().to(out.device)]
+    assert_attention_close(got, ref, wl.dtype, "config 4 prompt rows fp8")
