@@ -1721,9 +1721,12 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
   int32_t st = split_tokens;
   if (st == 0) {
     // Partition long decode contexts only when the batch alone cannot fill
-    // the chip: aim for ~2048 workgroups of at least 256 tokens each.
+    // the chip: aim for ~2048 workgroups of at least 256 tokens each.  A
+    // batch of one request with more query rows than one decode tile holds
+    // no decode item, so it gets no partitions (and no reduce launch).
     const int64_t want = 2048;
-    if (pairs_per_req >= want || max_seq_len <= 256) {
+    const bool one_prompt = num_reqs == 1 && (int64_t)max_query_len * p.group > kPairsPerTile;
+    if (pairs_per_req >= want || max_seq_len <= 256 || one_prompt) {
       st = ((std::max(max_seq_len, 1) + 31) / 32) * 32;
     } else {
       const int64_t per = ((int64_t)max_seq_len * pairs_per_req + want - 1) / want;
