@@ -155,6 +155,15 @@ def test_workspace_sizes():
     # forcing partitions adds partial-result storage
     assert ws(16, 16, 64, 8, 128, 1, 32768, split_tokens=1024) > ws(16, 16, 64, 8, 128, 1, 32768,
                                                                     split_tokens=32768)
+    # one request with more query rows than a decode tile: no partitions, so
+    # the workspace holds only the work list (the default for two such
+    # requests, which may hide a decode, partitions the contexts)
+    one = ws(1, 5000, 32, 8, 128, 5000, 8000)
+    assert one == ws(1, 5000, 32, 8, 128, 5000, 8000, split_tokens=8000)
+    assert ws(2, 5000, 32, 8, 128, 5000, 8000) > ws(2, 5000, 32, 8, 128, 5000, 8000,
+                                                    split_tokens=8000)
+    # one request of 4 rows at G = 4 is a decode item: partitions as before
+    assert ws(1, 4, 32, 8, 128, 4, 8000) > ws(1, 4, 32, 8, 128, 4, 8000, split_tokens=8000)
     # every configuration's workspace is modest next to HBM
     assert ws(17, 2064, 64, 8, 128, 2048, 32768) < (256 << 20)
     assert ws(201, 5200, 32, 8, 128, 5000, 8192) < (256 << 20)
