@@ -65,6 +65,11 @@ MUTANTS = {
     "zeroing skips the value pool": ("memset(value_cache + (int64_t)block_ids[k] * block_bytes, 0, (size_t)block_bytes);",
                                      "(void)0;"),
     "fp8 value layout collides": ("* 4 + (dim / 16) % 4) * 4 + tok % 4;", "* 4 + (dim / 32) % 4) * 4 + tok % 4;"),
+    "fp8 value dim and token fields swapped": ("* 4 + (dim / 16) % 4) * 4 + tok % 4;",
+                                               "* 4 + tok % 4) * 4 + (dim / 16) % 4;"),
+    "fp8 key stored dim-major": (
+        "int32_t head_dim) {\n  return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;\n}\n\n/* Byte of (block, head, token, dim) in an FP8 V pool",
+        "int32_t head_dim) {\n  return ((block * num_kv_heads + head) * head_dim + dim) * (int64_t)block_size + tok;\n}\n\n/* Byte of (block, head, token, dim) in an FP8 V pool"),
 }
 
 

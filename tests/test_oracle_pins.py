@@ -681,6 +681,44 @@ def test_fp8_value_layout_fills_every_byte_of_a_run():
     assert (vc != 0).all() and (kc != 0).all()
 
 
+def _fp8_distinct_codes(d):
+    """Codes for dims 0..d-1 of one row, all different, none zero or NaN:
+    0x01..0x7E, then negative codes."""
+    pos = list(range(0x01, 0x7F))
+    return np.array((pos + [0x80 | c for c in pos])[:d], np.uint8)
+
+
+def test_fp8_pool_byte_positions():
+    """Where one token's K and V rows land in the FP8 pools, byte by byte, for
+    every token position of a block and both heads of a two-head pool, written
+    out from the documented orders: K token-major
+    [block][head][token][dim]; each V (block, head) run ordered
+    [dim / 64][token / 4][dim % 16][(dim / 16) % 4][token % 4].  Each element
+    of the row is the exact value of a distinct code (scale 1), so its byte is
+    found wherever it lands."""
+    H, d, bs, nb = 2, 128, 16, 3
+    codes = [_fp8_distinct_codes(d), np.roll(_fp8_distinct_codes(d), 37)]
+    vals = np.array([[oracle.fp8_decode(int(c)) for c in codes[h]] for h in range(H)])
+    row = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16)[None]  # exact in bf16
+    assert np.array_equal(row.float().numpy()[0], vals)
+    filler = 0xFF  # a NaN code: no finite value encodes to it
+    for tok in range(bs):
+        blk = 1
+        kc = np.full((nb, H, bs, d), filler, np.uint8)
+        vc = np.full((nb, H, d * bs), filler, np.uint8)
+        oracle.kv_write_fp8(row, row, kc, vc, [blk * bs + tok], bs, 1.0, 1.0)
+        kflat, vflat = kc.reshape(-1), vc.reshape(-1)
+        for h in range(H):
+            run = (blk * H + h) * d * bs
+            for dim in range(d):
+                k_at = ((blk * H + h) * bs + tok) * d + dim
+                v_at = run + (dim // 64) * 1024 + (tok // 4) * 256 + (dim % 16) * 16 + \
+                    ((dim // 16) % 4) * 4 + tok % 4
+                assert kflat[k_at] == codes[h][dim], ("K", tok, h, dim)
+                assert vflat[v_at] == codes[h][dim], ("V", tok, h, dim)
+        assert int((kc != filler).sum()) == H * d and int((vc != filler).sum()) == H * d
+
+
 def test_fp8_write_rejects_bad_arguments():
     key, value, slots, nb = _fp8_case(5)
     kc = np.zeros((nb, 2, 16, 128), np.uint8)
