@@ -2,19 +2,27 @@
 
 A step is the whole hot path over one batch: prepare_inputs (flat-batch
 indices and slot mapping) -> kv_cache_write (this step's K/V rows into the
-block pool) -> paged_attention_varlen (plan, main, and the split-KV reduce
-when a context is partitioned).  Inputs are resident in HBM before timing;
-outputs, workspace and index buffers are preallocated, so a step allocates
-nothing.
+block pool) -> the attention plan (the work list) -> the attention run (main
+kernel, and the split-KV reduce when a context is partitioned).  Plan then
+run is the same work as one paged_attention_varlen call.  Inputs are
+resident in HBM before timing; outputs, workspace and index buffers are
+preallocated, so a step allocates nothing.
 
-Default workload: the 13B-shaped decode batch (64 requests x 1 token,
-context lengths uniform in [512, 2048], 40 q / 40 kv heads, head_dim 128,
-bf16, 16-token blocks scattered in a pool 1.25x the need).  ``--workload``
-selects another of the five configurations.
+Default workload: the mixed chunked-prefill step ("Building the Batch", "Why
+flatten": one 5,000-token prompt chunk with 3,000 tokens already computed,
+next to 200 single-token decodes with contexts uniform in [1024, 8192]; 32 q
+/ 8 kv heads, head_dim 128, bf16, 16-token blocks placed at random), the
+largest of the five configurations.  ``--workload`` selects another.
 
-Prints one JSON line: tokens/s of the whole step, the roofline of the
-attention call (HBM-bound for decode batches, MFMA-bound for prompt chunks),
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+Timing protocol: every timed iteration starts after a 512 MiB write that
+flushes L2 and the MALL, and is bracketed by HIP events on the stream the
+library launches on; medians, p10 and p90 are reported, and the GPU clocks are
+sampled while the loops run.  The roofline is that of the attention run
+(max(t_bytes, t_flops) / t), for the whole batch and for its decode rows and
+prompt rows alone over the same pools.
+
+Prints one JSON line: tokens/s of the whole step, the roofline figures, and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -41,22 +49,24 @@ FP8_SCALES = (0.0125, 0.0125)    # k_scale, v_scale of --kv-dtype fp8 (N(0,1) hi
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     p.add_argument("--rows", default="all", choices=["all", "decode", "prefill"],
                    help="time the whole batch, or only its single-token/short (decode) "
                         "or prompt-chunk (prefill) requests over the same pools")
     p.add_argument("--split-tokens", type=int, default=0,
                    help="context partition size of decode items (0 = library default)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="approximate budget of the CPU oracle baseline")
+                   help="approximate budget of the CPU oracle baseline (all threads)")
+    p.add_argument("--cpu-single-seconds", type=float, default=5.0,
+                   help="approximate budget of the single-thread CPU oracle baseline")
     p.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                    help="cache element type: bf16, or FP8 E4M3 codes with per-pool scales "
                         "(the same history quantised; q and out stay bf16)")
     p.add_argument("--graph", action="store_true",
-                   help="also capture the step in a HIP graph and time K replays; value and "
-                        "ms_per_step then come from the replays")
+                   help="also capture the step in a HIP graph and time K replays (reported "
+                        "beside the eager figures)")
     p.add_argument("--op", default="step", choices=["step", "input_ids", "copy_blocks",
                                                      "zero_blocks"],
                    help="step: the hot path above.  input_ids: prepare_inputs + "
@@ -162,14 +172,28 @@ def measured_traffic(key, which=TRAFFIC):
     return int(kv[key])
 
 
-def cpu_baseline(wl, budget_s):
-    """The fp64 oracle timed on host cores on a bounded sample of the same step.
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s, single_s):
+    """The fp64 oracle, as it is, timed on host cores on a bounded sample of
+    the same step, phase by phase.
 
     prepare and the KV write run on the whole batch; attention runs on an
-    evenly strided sample of rows (so prompt-chunk and decode rows appear in
-    the batch's proportions), sized by a short calibration run to take about
-    ``budget_s``.  Rate = sampled rows / (attention time of the sample +
-    prepare and write time prorated to the sample)."""
+    evenly strided sample of rows (prompt-chunk and decode rows in the batch's
+    proportions), sized by a short calibration run to take about
+    ``budget_s`` with every OpenMP thread, then a smaller sample on one
+    thread for about ``single_s``.  Rate = sampled rows / (attention time of
+    the sample + prepare and write time scaled to the sample's share of the
+    rows)."""
     import oracle
     T = wl.num_tokens
     kc, vc = wl.key_cache.cpu(), wl.value_cache.cpu()
@@ -178,38 +202,143 @@ def cpu_baseline(wl, budget_s):
     t0 = time.perf_counter()
     prep = oracle.prepare(wl.num_scheduled_tokens, wl.num_computed_tokens, wl.block_table,
                           wl.block_size, wl.num_blocks)
+    t_prep = time.perf_counter() - t0
+    t0 = time.perf_counter()
     if wl.kv_scales is None:
         oracle.kv_write(key, val, kc, vc, prep["slot_mapping"], wl.block_size)
     else:
         oracle.kv_write_fp8(key, val, kc, vc, prep["slot_mapping"], wl.block_size, *wl.kv_scales)
-    t_pw = time.perf_counter() - t0
+    t_write = time.perf_counter() - t0
 
-    def attn(rows):
+    def attn(rows, nthreads):
         t1 = time.perf_counter()
         oracle.attention(q, kc, vc, prep["query_start_loc"], prep["seq_lens"], wl.block_table,
-                         wl.block_size, wl.scale, rows=rows, kv_scales=wl.kv_scales)
+                         wl.block_size, wl.scale, rows=rows, kv_scales=wl.kv_scales,
+                         num_threads=nthreads)
         return time.perf_counter() - t1
 
-    n = min(T, 2 * threads)
-    rows = np.linspace(0, T - 1, n).astype(np.int32)
-    dt = attn(rows)
-    while n < T and dt < budget_s / 3:
-        n = min(T, max(n + 1, int(n * min(16.0, 0.8 * budget_s / max(dt, 1e-3)))))
+    def sample(budget, nthreads):
+        n = min(T, max(2, 2 * nthreads))
         rows = np.unique(np.linspace(0, T - 1, n).astype(np.int32))
+        dt = attn(rows, nthreads)
+        while len(rows) < T and dt < budget / 3:
+            n = min(T, max(len(rows) + 1, int(len(rows) * min(16.0, 0.8 * budget /
+                                                              max(dt, 1e-3)))))
+            rows = np.unique(np.linspace(0, T - 1, n).astype(np.int32))
+            dt = attn(rows, nthreads)
+        reps = 1
+        if len(rows) == T:  # the whole batch is cheap: repeat it for a stable time
+            while dt < budget / 3 and reps < 1000:
+                dt += attn(rows, nthreads)
+                reps += 1
         n = len(rows)
-        dt = attn(rows)
-    reps = 1
-    if n == T:  # the whole batch is cheap: repeat it for a stable time
-        while dt < budget_s / 3 and reps < 1000:
-            dt += attn(rows)
-            reps += 1
-    total = dt + t_pw * reps * n / T
-    what = (f"all {T} rows, {reps} times" if reps > 1 else
-            f"{n} evenly strided rows of {T}")
-    return {"value": round(reps * n / total, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"prepare + kv_write on all {T} rows ({t_pw:.2f} s, prorated), attention "
-                      f"on {what} ({dt:.2f} s); fp64"}
+        total = dt + (t_prep + t_write) * reps * n / T
+        what = (f"all {T} rows, {reps} times" if reps > 1 else f"{n} evenly strided rows of {T}")
+        return reps * n / total, dt, what
+
+    rate, dt, what = sample(budget_s, threads)
+    rate1, dt1, what1 = sample(single_s, 1)
+    return {"value": round(rate, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"fp64 oracle; prepare ({t_prep:.3f} s) and kv_write ({t_write:.3f} s) "
+                      f"on all {T} rows, prorated; attention on {what} ({dt:.2f} s)",
+            "phases_s": {"prepare": round(t_prep, 4), "kv_write": round(t_write, 4),
+                         "attention_sample": round(dt, 3)},
+            "single_thread": {"value": round(rate1, 2), "unit": "tokens/s", "cores": 1,
+                              "sample": f"attention on {what1} ({dt1:.2f} s), prepare and "
+                                        f"kv_write prorated"}}
+
+
+class ClockReader:
+    """SCLK / MCLK of the GPU (amdsmi's clock query; sysfs pp_dpm_* as a
+    fallback).  ``under_load`` samples them while a long queue of the
+    benchmark's own kernels runs.  Never fails the benchmark: where neither
+    source is readable it reports that."""
+
+    def __init__(self):
+        self.source = None
+        try:
+            self._read = self._init_reader()
+        except Exception:
+            self._read = None
+
+    def _init_reader(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            h = handles[0]
+            try:
+                import torch
+                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+                for cand in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(cand)
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        h = cand
+            except Exception:
+                pass
+
+            def read():
+                g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]
+                m = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"]
+                return float(g), float(m)
+            read()
+            self.source = "amdsmi_get_clock_info (GFX, MEM)"
+            return read
+        except Exception:
+            pass
+        import glob
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            sc, mc = os.path.join(dev, "pp_dpm_sclk"), os.path.join(dev, "pp_dpm_mclk")
+
+            def cur(path):
+                with open(path) as fh:
+                    for line in fh:
+                        if "*" in line:
+                            return float(line.split(":")[1].strip().rstrip("*").strip()
+                                         .lower().replace("mhz", ""))
+                raise ValueError(path)
+            try:
+                def read(sc=sc, mc=mc):
+                    return cur(sc), cur(mc)
+                read()
+                self.source = f"{sc} and pp_dpm_mclk"
+                return read
+            except Exception:
+                continue
+        return None
+
+    def under_load(self, enqueue, done, period_s=0.01):
+        """Call ``enqueue`` (which queues GPU work without waiting), then read
+        the clocks every ``period_s`` until ``done()`` is true."""
+        if self._read is None:
+            enqueue()
+            return {"source": None, "note": "no clock source readable"}
+        sclk, mclk = [], []
+        enqueue()
+        t_end = time.perf_counter() + 30.0
+        while not done() and time.perf_counter() < t_end:
+            try:
+                g, m = self._read()
+                sclk.append(g)
+                mclk.append(m)
+            except Exception:
+                pass
+            time.sleep(period_s)
+        if not sclk:
+            return {"source": self.source, "note": "no readings while the kernels ran"}
+        return {"source": self.source, "samples": len(sclk),
+                "sclk_mhz": {"median": float(np.median(sclk)), "min": float(np.min(sclk)),
+                             "max": float(np.max(sclk))},
+                "mclk_mhz": {"median": float(np.median(mclk)), "min": float(np.min(mclk)),
+                             "max": float(np.max(mclk))}}
+
+
+def pct(xs):
+    xs = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(xs)), 4), "p10": round(float(np.percentile(xs, 10)), 4),
+            "p90": round(float(np.percentile(xs, 90)), 4), "mean": round(float(xs.mean()), 4),
+            "n": int(xs.size)}
 
 
 def _timed_launches(fn, steps, warmup):
@@ -360,11 +489,96 @@ def bench_op(args):
     print(json.dumps(line), flush=True)
 
 
+def step_buffers(wl, split_tokens):
+    """Device inputs and preallocated outputs / workspace of one step of ``wl``."""
+    import torch
+    import paged_kv_cache_prepare_amd as pkv
+    dev = wl.q.device
+    T, R = wl.num_tokens, wl.num_reqs
+    i32 = dict(dtype=torch.int32, device=dev)
+    b = {"nst": torch.from_numpy(wl.num_scheduled_tokens).to(dev),
+         "nct": torch.from_numpy(wl.num_computed_tokens).to(dev),
+         "bt": torch.from_numpy(wl.block_table).to(dev),
+         "prep": {"req_indices": torch.empty(T, **i32), "positions": torch.empty(T, **i32),
+                  "slot_mapping": torch.empty(T, dtype=torch.int64, device=dev),
+                  "query_start_loc": torch.empty(R + 1, **i32),
+                  "seq_lens": torch.empty(R, **i32), "logits_indices": torch.empty(R, **i32)},
+         "out": torch.empty_like(wl.q), "ks": None, "vs": None}
+    if wl.kv_scales is not None:
+        b["ks"] = torch.tensor([wl.kv_scales[0]], dtype=torch.float32, device=dev)
+        b["vs"] = torch.tensor([wl.kv_scales[1]], dtype=torch.float32, device=dev)
+    need = pkv.attention_workspace_bytes(R, T, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                         wl.max_query_len, wl.max_seq_len, split_tokens, wl.dtype)
+    b["ws"] = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    return b
+
+
+def make_phases(wl, b, split_tokens):
+    """The step's calls: prepare_inputs, kv_cache_write, the attention plan and
+    the attention run (main + reduce) over that plan.  Plan followed by run is
+    the same work as one paged_attention_varlen call."""
+    import paged_kv_cache_prepare_amd as pkv
+    prep = b["prep"]
+    kc, vc = wl.key_cache, wl.value_cache
+
+    def prepare():
+        pkv.prepare_inputs(b["nst"], b["nct"], b["bt"], num_tokens=wl.num_tokens,
+                           block_size=wl.block_size, num_blocks=wl.num_blocks, out=prep)
+
+    def write():
+        if b["ks"] is None:
+            pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"],
+                               block_size=wl.block_size)
+        else:
+            pkv.kv_cache_write_fp8(wl.key, wl.value, kc, vc, prep["slot_mapping"], b["ks"],
+                                   b["vs"], block_size=wl.block_size)
+
+    def plan():
+        pkv.paged_attention_plan(prep["query_start_loc"], prep["seq_lens"],
+                                 num_tokens=wl.num_tokens, num_q_heads=wl.num_q_heads,
+                                 num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
+                                 max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                                 dtype=wl.dtype, split_tokens=split_tokens, workspace=b["ws"])
+
+    def run():
+        pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], b["bt"],
+                            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                            scale=wl.scale, out=b["out"], split_tokens=split_tokens,
+                            workspace=b["ws"], k_scale=b["ks"], v_scale=b["vs"], planned=True)
+
+    return prepare, write, plan, run
+
+
+def roofline_of(work, t_ms):
+    """Fraction of the roofline for the attention work ``work`` done in
+    ``t_ms``: the bound is max(t_bytes, t_flops) with t_bytes = unique
+    algorithmic bytes / HBM peak and t_flops = visible-pair flops / bf16 MFMA
+    peak; achieved is reported in the unit of the larger one."""
+    t = t_ms / 1e3
+    flops = work["flops_decode"] + work["flops_prefill"]
+    t_bytes = work["bytes_unique"] / (HBM_PEAK_GBS * 1e9)
+    t_flops = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_flops > t_bytes:
+        ach = flops / t / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = work["bytes_unique"] / t / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4)}
+    r.update({"algorithmic_bytes": work["bytes_unique"], "algorithmic_flops": flops,
+              "avg_ms": round(t_ms, 4), "hbm_gbs": round(work["bytes_unique"] / t / 1e9, 1),
+              "tflops": round(flops / t / 1e12, 2),
+              "t_bytes_ms": round(t_bytes * 1e3, 4), "t_flops_ms": round(t_flops * 1e3, 4)})
+    return r
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path.", file=sys.stderr)
+              "multi-GPU path: the hot path is measured on one GPU's share at its real shape.",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
@@ -373,107 +587,119 @@ def main():
         bench_op(args)
         return
     import torch
-    import paged_kv_cache_prepare_amd as pkv
     from paged_kv_cache_prepare_amd import workloads
 
     dev = torch.device("cuda:0")
-    wl = workloads.config(args.workload, device=dev)
+    full = workloads.config(args.workload, device=dev)
     if args.kv_dtype == "fp8":
-        if wl.dtype != torch.bfloat16:
+        if full.dtype != torch.bfloat16:
             print("an FP8 cache needs bf16 queries (workloads 2-5)", file=sys.stderr)
             sys.exit(2)
-        wl = workloads.to_fp8(wl, *FP8_SCALES)
+        full = workloads.to_fp8(full, *FP8_SCALES)
+    group = full.num_q_heads // full.num_kv_heads
+    short = full.num_scheduled_tokens * group <= 16
+    subs = {"decode": np.nonzero(short)[0], "prefill": np.nonzero(~short)[0]}
+    wl = full
     if args.rows != "all":
-        group = wl.num_q_heads // wl.num_kv_heads
-        short = wl.num_scheduled_tokens * group <= 16
-        keep = np.nonzero(short if args.rows == "decode" else ~short)[0]
-        if len(keep) == 0:
+        if len(subs[args.rows]) == 0:
             print(f"workload {args.workload} has no {args.rows} rows", file=sys.stderr)
             sys.exit(2)
-        wl = workloads.select(wl, keep)
+        wl = workloads.select(full, subs[args.rows])
     work = algorithmic_work(wl)
-    T, R = wl.num_tokens, wl.num_reqs
-    nst = torch.from_numpy(wl.num_scheduled_tokens).to(dev)
-    nct = torch.from_numpy(wl.num_computed_tokens).to(dev)
-    bt = torch.from_numpy(wl.block_table).to(dev)
-    i32 = dict(dtype=torch.int32, device=dev)
-    prep = {"req_indices": torch.empty(T, **i32), "positions": torch.empty(T, **i32),
-            "slot_mapping": torch.empty(T, dtype=torch.int64, device=dev),
-            "query_start_loc": torch.empty(R + 1, **i32), "seq_lens": torch.empty(R, **i32),
-            "logits_indices": torch.empty(R, **i32)}
-    kc, vc = wl.key_cache, wl.value_cache
-    ks = vs = None
-    if wl.kv_scales is not None:
-        ks = torch.tensor([wl.kv_scales[0]], dtype=torch.float32, device=dev)
-        vs = torch.tensor([wl.kv_scales[1]], dtype=torch.float32, device=dev)
-    out = torch.empty_like(wl.q)
-    ws_bytes = pkv.attention_workspace_bytes(R, T, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                             wl.max_query_len, wl.max_seq_len, args.split_tokens,
-                                             wl.dtype)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    T = wl.num_tokens
     stream = torch.cuda.current_stream(dev)
+    # the cache flush: a 512 MiB write (twice the 256 MB MALL) before every timed
+    # iteration, outside the event brackets, so no timed call finds the pools
+    # in L2 or the MALL from the previous iteration
+    scratch = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
 
-    def step(ev_attn=None, ev_phase=None):
-        """One step.  ev_attn: events around the attention call; ev_phase:
-        events before prepare and before the KV write (phase pass only)."""
-        if ev_phase is not None:
-            ev_phase[0].record(stream)
-        pkv.prepare_inputs(nst, nct, bt, num_tokens=T, block_size=wl.block_size,
-                           num_blocks=wl.num_blocks, out=prep)
-        if ev_phase is not None:
-            ev_phase[1].record(stream)
-        if ks is None:
-            pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep["slot_mapping"],
-                               block_size=wl.block_size)
-        else:
-            pkv.kv_cache_write_fp8(wl.key, wl.value, kc, vc, prep["slot_mapping"], ks, vs,
-                                   block_size=wl.block_size)
-        if ev_attn is not None:
-            ev_attn[0].record(stream)
-        pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
-                            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
-                            scale=wl.scale, out=out, split_tokens=args.split_tokens,
-                            workspace=ws, k_scale=ks, v_scale=vs)
-        if ev_attn is not None:
-            ev_attn[1].record(stream)
+    def flush():
+        scratch.fill_(1.0)
 
-    def new_events(n, per):
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(per)] for _ in range(n)]
+    b = step_buffers(wl, args.split_tokens)
+    prepare, write, plan, run = make_phases(wl, b, args.split_tokens)
+
+    def step():
+        prepare()
+        write()
+        plan()
+        run()
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
     for _ in range(args.warmup):
+        flush()
         step()
-    # timed region: only the attention call (the roofline kernel) is bracketed
-    # by events; every event record costs the stream a few microseconds
-    events = new_events(args.steps, 2)
+    clock_reader = ClockReader()
+    # timed region: K steps, each after a flush, each bracketed by events
+    ev = [events(2) for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        flush()
+        ev[k][0].record(stream)
+        step()
+        ev[k][1].record(stream)
     torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-    t_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    # phase pass (untimed): prepare and KV-write times from events around each
-    phase_steps = min(args.steps, 20)
-    ph_ev, at_ev = new_events(phase_steps, 2), new_events(phase_steps, 2)
-    for k in range(phase_steps):
-        step(at_ev[k], ph_ev[k])
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    # phase pass, same protocol: events between the calls
+    ph = [events(5) for _ in range(args.steps)]
+    for k in range(args.steps):
+        flush()
+        ph[k][0].record(stream)
+        prepare()
+        ph[k][1].record(stream)
+        write()
+        ph[k][2].record(stream)
+        plan()
+        ph[k][3].record(stream)
+        run()
+        ph[k][4].record(stream)
     torch.cuda.synchronize(dev)
-    t_prep = float(np.mean([e[0].elapsed_time(e[1]) for e in ph_ev]))
-    t_write = float(np.mean([p[1].elapsed_time(a[0]) for p, a in zip(ph_ev, at_ev)]))
-    # the attention call without its planning step (pkv_paged_attention_run over
-    # the work list the last step left in the workspace): what each further
-    # layer of a model pays for the same batch
-    run_ev = new_events(phase_steps, 2)
-    for k in range(phase_steps):
-        run_ev[k][0].record(stream)
-        pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
-                            max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
-                            scale=wl.scale, out=out, split_tokens=args.split_tokens,
-                            workspace=ws, k_scale=ks, v_scale=vs, planned=True)
-        run_ev[k][1].record(stream)
+    phase_ms = {name: [e[i].elapsed_time(e[i + 1]) for e in ph]
+                for i, name in enumerate(("prepare", "kv_write", "plan", "run"))}
+    # the decode rows and the prompt rows alone over the same pools: the
+    # per-path fractions (same protocol, attention run only)
+    sub_lines = {}
+    if args.rows == "all":
+        for name, reqs in subs.items():
+            if len(reqs) == 0 or len(reqs) == wl.num_reqs:
+                continue
+            sw = workloads.select(full, reqs)
+            sb = step_buffers(sw, args.split_tokens)
+            s_prep, _, s_plan, s_run = make_phases(sw, sb, args.split_tokens)
+            s_prep()
+            s_plan()
+            for _ in range(max(2, args.warmup // 2)):
+                flush()
+                s_run()
+            sev = [events(2) for _ in range(args.steps)]
+            for k in range(args.steps):
+                flush()
+                sev[k][0].record(stream)
+                s_run()
+                sev[k][1].record(stream)
+            torch.cuda.synchronize(dev)
+            ms = pct([e[0].elapsed_time(e[1]) for e in sev])
+            sr = roofline_of(algorithmic_work(sw), ms["median"])
+            sub_lines[name] = {"rows": sw.num_tokens, "requests": sw.num_reqs,
+                               "run_ms": ms, **sr}
+            del sb
+
+    # clocks while the attention run executes: 300 runs queued back to back
+    # (no flush), read until the last one ends
+    done_ev = torch.cuda.Event()
+
+    def enqueue():
+        for _ in range(300):
+            run()
+        done_ev.record(stream)
+
+    clocks = clock_reader.under_load(enqueue, done_ev.query)
+    clocks["note"] = "sampled while 300 attention runs of the workload executed back to back"
     torch.cuda.synchronize(dev)
-    t_run = float(np.mean([e[0].elapsed_time(e[1]) for e in run_ev]))
 
     graph_ms = None
     if args.graph:
@@ -486,70 +712,64 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
-        for _ in range(args.warmup):
+        gms = []
+        for k in range(args.warmup + args.steps):
+            flush()
+            e0, e1 = events(2)
+            e0.record(stream)
             graph.replay()
-        torch.cuda.synchronize(dev)
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize(dev)
-        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        eager_ms, ms_step = ms_step, graph_ms
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            if k >= args.warmup:
+                gms.append(e0.elapsed_time(e1))
+        graph_ms = pct(gms)
 
-    attn_s = t_attn / 1e3
-    flops = work["flops_decode"] + work["flops_prefill"]
-    gbs = work["bytes_unique"] / attn_s / 1e9
-    tflops = flops / attn_s / 1e12
-    if work["flops_prefill"] > work["flops_decode"] and \
-            flops / MFMA_BF16_PEAK_TFLOPS / 1e12 > work["bytes_unique"] / HBM_PEAK_GBS / 1e9:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    st = pct(step_ms)
+    run_ms = pct(phase_ms["run"])
+    roof = roofline_of(work, run_ms["median"])
     key = f"w{args.workload}_{args.rows}_split{args.split_tokens}"
     roof["traffic"] = measured_traffic(key + ("_fp8" if args.kv_dtype == "fp8" else ""))
-    roof["kernel"] = "paged_attention_varlen (plan + attn_main + reduce), HIP events"
-    roof["algorithmic_bytes"] = work["bytes_unique"]
-    roof["algorithmic_flops"] = flops
-    roof["avg_ms"] = round(t_attn, 4)
+    roof["kernel"] = ("attn_main_kernel + attn_reduce_kernel (pkv_paged_attention_run over "
+                      "the step's plan), HIP events, median of the timed iterations, each after "
+                      "a 512 MiB cache flush")
+    roof["rule"] = "frac = max(t_bytes, t_flops) / t"
+    if sub_lines:
+        roof["sub_batches"] = sub_lines
 
-    cpu = cpu_baseline(wl, args.cpu_seconds)
+    cpu = cpu_baseline(wl, args.cpu_seconds, args.cpu_single_seconds)
     line = {
         "metric": METRIC,
-        "value": round(T / (ms_step / 1e3), 1),
+        "value": round(T / (st["median"] / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": st["median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("bf16" if wl.dtype == torch.bfloat16 else "f32") +
                  ("+fp8kv" if args.kv_dtype == "fp8" else ""),
         "data": "synthetic (seeded N(0,1) K/V/Q, random block placement)",
-        "config": {"workload": workloads.CONFIG_NAMES[args.workload], "num_reqs": R,
+        "config": {"workload": workloads.CONFIG_NAMES[args.workload], "num_reqs": wl.num_reqs,
                    "num_tokens": T, "context_tokens": work["context_tokens"],
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "seed": wl.seed,
                    "split_tokens": args.split_tokens, "rows": args.rows,
                    "kv_dtype": args.kv_dtype},
-        "phases_ms": {"prepare": round(t_prep, 4), "kv_write": round(t_write, 4),
-                      "attention": round(t_attn, 4),
-                      "attention_run_only": round(t_run, 4),
-                      "note": "attention from events in the timed region; prepare, kv_write "
-                              "and attention_run_only (the call without re-planning, as every "
-                              "further layer of a model step runs it) from separate passes"},
-        "context_tokens_per_s": round(work["context_tokens"] / (ms_step / 1e3), 1),
-        "attention_hbm_gbs": round(gbs, 1),
-        "attention_tflops": round(tflops, 3),
+        "timing": {"protocol": "each of the K timed steps runs after a 512 MiB write (L2 and "
+                               "MALL flush) and is bracketed by HIP events on the library's "
+                               "stream; value = num_tokens / median step time",
+                   "step_ms": st, "wall_ms_per_iteration_with_flush": round(wall_ms, 4)},
+        "phases_ms": {name: pct(v) for name, v in phase_ms.items()},
+        "context_tokens_per_s": round(work["context_tokens"] / (st["median"] / 1e3), 1),
         "roofline": roof,
+        "clocks": clocks,
         "cpu_baseline": cpu,
     }
     if graph_ms is not None:
-        line["graph"] = {"ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(eager_ms, 4),
-                         "note": "value and ms_per_step come from HIP-graph replays of the step"}
+        line["graph"] = {"step_ms": graph_ms,
+                         "note": "HIP-graph replays of the step, same flush protocol"}
     print(json.dumps(line), flush=True)
 
 

@@ -38,9 +38,11 @@
  *   device can address) owned by the caller.  The library allocates nothing,
  *   keeps no device state between calls, never synchronises, never reads
  *   device memory from the host, and only enqueues work on `stream`
- *   (a hipStream_t; NULL means the default stream).  Calls are reentrant.
+ *   (a hipStream_t; NULL means the default stream).  Calls are reentrant:
+ *   host threads may call any entry point concurrently.
  *   (The checked build is the exception: it reads a check word back and
- *   synchronises `stream` once per call.)
+ *   synchronises `stream` once per call, and its calls share one device
+ *   check word, so checked calls must not run concurrently.)
  * - Host-side validation covers the scalar arguments and null pointers only;
  *   it returns a status and enqueues nothing on failure.  Device-side
  *   contents are preconditions (listed per call).  Where a precondition on
@@ -336,7 +338,12 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
  *   key_cache, value_cache  the K and V pools, num_blocks blocks each
  *   out             [num_tokens][num_q_heads][head_dim] of `dtype`, row stride
  *                   out_row_stride elements, 16-byte aligned rows (written)
- *   query_start_loc int32 [num_reqs + 1], non-decreasing, last = num_tokens
+ *   query_start_loc int32 [num_reqs + 1], non-decreasing, last <= num_tokens;
+ *                   rows from query_start_loc[num_reqs] to num_tokens - 1
+ *                   are padding rows of a step captured at a fixed size
+ *                   ("Building the Batch", "Padding, after all that"): they
+ *                   belong to no request and the bf16 path leaves their
+ *                   output untouched (the fp32 path writes zeros there)
  *   seq_lens        int32 [num_reqs]
  *   block_table     int32 [num_reqs][bt_row_stride]; request r reads columns
  *                   0 .. ceil(seq_lens[r] / block_size) - 1, all < bt_row_stride

@@ -299,6 +299,7 @@ static pkv_status attention_call(
   const int32_t* planned =
       mode == AttnMode::kRun && plan.total_bytes > 0 ? static_cast<const int32_t*>(workspace)
                                                      : nullptr;
+  (void)planned;  // read by the checked build only
   PKV_CHECK(pkv::check_attention(query_start_loc, seq_lens, runs ? block_table : nullptr,
                                  bt_row_stride, num_reqs, num_tokens, max_query_len, max_seq_len,
                                  num_blocks, a.k_scale, a.v_scale, planned, fp, s));

@@ -37,6 +37,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "pkv_internal.h"
 
@@ -52,19 +53,21 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPrefillItemsWord = 4;  // workspace header word: prefill items at the list head
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device, cached per device id.  Concurrent
+// first calls from several host threads may each query the device; they
+// store the same value, and the atomics make that race benign.
 int device_cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];  // static storage: zero-initialised
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 constexpr int kThreads = kWaves * 64;
 
@@ -186,16 +189,6 @@ __device__ inline int upper_bound_lds(const int* s, int n, int x) {
   return lo;
 }
 
-// First index in the non-increasing s[0..n) whose value is <= x (n if none).
-__device__ inline int first_not_above(const int* s, int n, int x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (s[mid] <= x) hi = mid; else lo = mid + 1;
-  }
-  return lo;
-}
-
 struct PlanSmem {
   int wave[16];
   int len[kPlanReqs];    // seq_len by request (ordered path)
@@ -203,8 +196,9 @@ struct PlanSmem {
   int req[kPlanReqs];    // request at rank j (ordered path) / unused (chunked path)
   int incl[kPlanReqs];   // inclusive prefix of per-slot unit counts
   int aux[kPlanReqs];    // per-slot split count or tile count
-  int dreq[kPlanReqs];   // decode requests in rank order
+  int dreq[kPlanReqs];   // decode requests by split count, largest first
   int dns[kPlanReqs];    // their split counts (non-increasing)
+  int gt[kPlanMaxSplits + 1];  // decode requests with more than k splits
   int pk[kPlanMaxSplits + 1];  // decode units before split index k
 };
 
@@ -294,8 +288,11 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     hist[tid] = 0;
     __syncthreads();
     // Rank by seq_len, longest first, as a bucket sort over 1024 buckets of
-    // the length range (the order within a bucket, and so the list's order,
-    // may vary between calls; no result depends on it).
+    // the length range.  The order within a bucket follows the atomics and
+    // may vary between calls: it only places prompt tiles, whose emission
+    // below takes any order, and decode requests are sorted again by their
+    // exact split count before pass 1 relies on an order.  No result depends
+    // on the list's order (every item writes its own rows or partition).
     const int top = max(max_len, 1);
     const int bucket = mine ? (int)((int64_t)(top - min(max(L, 0), top)) * (kPlanReqs - 1) / top)
                             : 0;
@@ -332,36 +329,54 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
       carry = total;
       pre_units = total;
     }
-    // pass 1: decode partitions, partition-major over the decode requests in rank order
+    // pass 1: decode partitions, partition-major.  The decode requests are
+    // put in order of their split count, largest first, by a counting sort
+    // over the counts 1..max_splits (equal counts keep no particular order).
+    // Then the requests that have a partition k are exactly the first gt[k]
+    // of them, gt[k] = #{decode requests with more than k splits}, and the
+    // units of partition index k are pk[k] .. pk[k+1]-1 with pk the prefix
+    // sum of gt.
     {
-      int ns = 0;
+      int ns = 0, rq = -1;
       if (tid < num_reqs) {
-        const int rq = sm.req[tid];
+        rq = sm.req[tid];
         plan_units_of(sm.qlen[rq], sm.len[rq], group, split_tokens, max_splits, 1, &ns);
       }
-      int nd;
-      const int ci = block_scan_1024(ns > 0 ? 1 : 0, sm.wave, &nd) - 1;
-      if (ns > 0) {
-        sm.dreq[ci] = sm.req[tid];
-        sm.dns[ci] = ns;
+      for (int v = tid; v <= max_splits; v += kPlanReqs) sm.gt[v] = 0;
+      __syncthreads();
+      if (ns > 0) atomicAdd(&sm.gt[ns], 1);  // histogram of the split counts
+      __syncthreads();
+      // suffix sums of the histogram: slot i of the scan holds count
+      // max_splits - i, two slots per thread (max_splits <= 2 * kPlanReqs)
+      {
+        const int i0 = 2 * tid, i1 = i0 + 1;
+        const int h0 = i0 < max_splits ? sm.gt[max_splits - i0] : 0;
+        const int h1 = i1 < max_splits ? sm.gt[max_splits - i1] : 0;
+        int tot;
+        const int excl = block_scan_1024(h0 + h1, sm.wave, &tot) - h0 - h1;
+        __syncthreads();  // every histogram read is done
+        if (i0 < max_splits) sm.gt[max_splits - i0] = excl;
+        if (i1 < max_splits) sm.gt[max_splits - i1] = excl + h0;
+        if (tid == 0) sm.gt[0] = tot;
       }
       __syncthreads();
-      // units with partition index k: decode requests whose split count exceeds k
-      int pcarry = 0;
-      if (max_splits == 1) {  // one partition each: nothing to count
-        pcarry = nd;
-        if (tid == 0) sm.pk[1] = nd;
-      } else {
-        for (int kb = 0; kb < max_splits; kb += kPlanReqs) {
-          const int k = kb + tid;
-          const int ck = k < max_splits ? first_not_above(sm.dns, nd, k) : 0;
-          int tot;
-          const int incl = block_scan_1024(ck, sm.wave, &tot);
-          if (k < max_splits) sm.pk[k + 1] = pcarry + incl;
-          pcarry += tot;
-        }
+      int pcarry;
+      {
+        const int k0 = 2 * tid, k1 = k0 + 1;
+        const int g0 = k0 < max_splits ? sm.gt[k0] : 0;
+        const int g1 = k1 < max_splits ? sm.gt[k1] : 0;
+        const int excl = block_scan_1024(g0 + g1, sm.wave, &pcarry) - g0 - g1;
+        if (k0 < max_splits) sm.pk[k0] = excl;
+        if (k1 < max_splits) sm.pk[k1] = excl + g0;
+        if (tid == 0) sm.pk[max_splits] = pcarry;
       }
-      if (tid == 0) sm.pk[0] = 0;
+      __syncthreads();  // every gt read is done before the cursors move
+      // place: the requests with count v take ranks gt[v] .. gt[v-1]-1
+      if (ns > 0) {
+        const int pos = atomicAdd(&sm.gt[ns], 1);
+        sm.dreq[pos] = rq;
+        sm.dns[pos] = ns;
+      }
       __syncthreads();
       const int base = (int)min(carry * H, max_items);
       const int n = (int)min((int64_t)pcarry * H, max_items - base);

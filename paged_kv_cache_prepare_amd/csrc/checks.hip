@@ -9,6 +9,8 @@
 // kernels when any check fails.  The failed checks are ORed into a device
 // word as PKV_CHECK_* bits (include/pkv.h).  Every check reads only inside
 // the buffers the entry point describes.
+#include <atomic>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void check_block_list_kernel(const int32_t* id
 
 constexpr int32_t kDupCheckRows = 1 << 16;
 
-uint32_t g_last_flags = 0u;
+std::atomic<uint32_t> g_last_flags{0u};  // host copy of the last failure
 
 // Reset the word, run `launch`, wait for the stream, report.
 template <typename F>
@@ -164,7 +166,7 @@ pkv_status run_check(hipStream_t stream, F launch) {
       hipStreamSynchronize(stream) != hipSuccess)
     return PKV_ERR_LAUNCH;
   if (flags != 0u) {
-    g_last_flags = flags;
+    g_last_flags.store(flags, std::memory_order_relaxed);
     return PKV_ERR_DEVICE_DATA;
   }
   return PKV_OK;
@@ -174,7 +176,7 @@ unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
 
-uint32_t last_check_flags() { return g_last_flags; }
+uint32_t last_check_flags() { return g_last_flags.load(std::memory_order_relaxed); }
 
 pkv_status check_prepare(const int32_t* nst, const int32_t* nct, const int32_t* block_table,
                          int64_t bt_stride, int32_t num_reqs, int32_t num_tokens,

@@ -48,7 +48,6 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
     int64_t num_blocks, const int64_t* __restrict__ slot_mapping, int32_t num_tokens,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
   using elem_t = typename std::conditional<E == 2, uint16_t, uint32_t>::type;
-  constexpr int kVecElems = 16 / E;
   __shared__ u32x4 s_v[kTileTokens * kMaxRowBytes / 16];
   __shared__ int64_t s_slot[kTileTokens];
 

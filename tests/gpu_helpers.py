@@ -42,7 +42,12 @@ def gpu_scales(wl):
 
 
 def gpu_step(wl, split_tokens=0):
-    """prepare -> kv_write -> attention on the GPU (pool copies are written)."""
+    """prepare -> kv_write -> attention on the GPU (pool copies are written).
+
+    The output and the attention workspace are filled with NaN (0xFF bytes)
+    beforehand, and every output row must come back finite: a row, tile or
+    partition that no kernel wrote (or that read a partial nobody wrote)
+    shows up here even where the oracle comparison samples rows."""
     prep, bt = gpu_prepare(wl)
     kc, vc = wl.key_cache.clone(), wl.value_cache.clone()
     ks, vs = gpu_scales(wl)
@@ -52,10 +57,19 @@ def gpu_step(wl, split_tokens=0):
     else:
         pkv.kv_cache_write_fp8(wl.key, wl.value, kc, vc, prep["slot_mapping"], ks, vs,
                                block_size=wl.block_size)
-    out = pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
-                              max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
-                              scale=wl.scale, split_tokens=split_tokens, k_scale=ks, v_scale=vs)
+    out = torch.full_like(wl.q, float("nan"))
+    need = pkv.attention_workspace_bytes(wl.num_reqs, wl.num_tokens, wl.num_q_heads,
+                                         wl.num_kv_heads, wl.head_dim, wl.max_query_len,
+                                         wl.max_seq_len, split_tokens, wl.dtype)
+    ws = torch.full((max(need, 256),), 0xFF, dtype=torch.uint8, device=wl.q.device)
+    pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                        max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
+                        scale=wl.scale, split_tokens=split_tokens, k_scale=ks, v_scale=vs,
+                        out=out, workspace=ws)
     torch.cuda.synchronize()
+    bad = (~torch.isfinite(out)).reshape(out.shape[0], -1).any(1).nonzero()
+    assert bad.numel() == 0, \
+        f"{wl.name}: {bad.numel()} output rows not finite, first {bad[:8].flatten().tolist()}"
     return prep, kc, vc, out
 
 

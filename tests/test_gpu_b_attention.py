@@ -1,6 +1,7 @@
 """GPU parity of pkv_paged_attention_varlen against the fp64 oracle, through
-the C ABI: the five named configurations at full size (sampled rows, in the
-launch configuration the benchmark times), and small cases that span several
+the C ABI: the five named configurations at full size (in the launch
+configuration the benchmark times; every output row must be written, every
+decode row and a row of every prompt tile is compared), and small cases that span several
 tiles with ragged tails, every GQA group size, both head sizes and dtypes,
 forced context partitions, NaN-poisoned pools and bad block ids."""
 import math
@@ -19,23 +20,42 @@ from gpu_helpers import (assert_attention_close, assert_prepare_equal, bits_view
 pytestmark = pytest.mark.gpu
 
 
-def sample_rows(wl, n_per_request=3, max_rows=48, seed=0):
-    """First, last and a random row of requests, capped; all rows when few."""
+PAIRS_PER_TILE = 16    # (row, q head) columns of a decode item
+PREFILL_PAIRS = 128    # (row, q head) pairs of one prompt tile of one kv head
+
+
+def sample_rows(wl, seed=0, small=64):
+    """Rows the full-size checks compare with the oracle: every row of a
+    decode request (q_len * G <= 16), and for each prompt chunk its first and
+    last rows plus one seeded random row from every 128-pair tile.  A row
+    covers all q heads, so every (kv head, row tile) item of the launch holds
+    a compared row.  Returns None (all rows) for batches of at most ``small``
+    rows; otherwise the rows, with the prompt tiles covered asserted equal to
+    the tiles launched."""
     T = wl.num_tokens
-    if T <= max_rows:
+    if T <= small:
         return None
+    G = wl.num_q_heads // wl.num_kv_heads
     rng = np.random.default_rng(seed)
-    qsl = np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)])
+    qsl = np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)]).astype(np.int64)
     rows = set()
-    reqs = np.nonzero(wl.num_scheduled_tokens)[0]
-    # every prefill request gets a spread of rows; decodes are sampled
-    for r in reqs:
+    tiles_launched = tiles_covered = 0
+    for r in range(wl.num_reqs):
         n = int(wl.num_scheduled_tokens[r])
-        if n > 1:
-            rows.update(int(x) for x in np.linspace(qsl[r], qsl[r + 1] - 1, 12).astype(int))
-    dec = [r for r in reqs if wl.num_scheduled_tokens[r] == 1]
-    for r in rng.permutation(dec)[:max_rows - len(rows)]:
-        rows.add(int(qsl[r]))
+        if n == 0:
+            continue
+        if n * G <= PAIRS_PER_TILE:
+            rows.update(range(int(qsl[r]), int(qsl[r + 1])))
+            continue
+        rows.update((int(qsl[r]), int(qsl[r + 1]) - 1))
+        n_tiles = -(-n * G // PREFILL_PAIRS)
+        tiles_launched += n_tiles
+        for t in range(n_tiles):
+            lo = PREFILL_PAIRS * t // G
+            hi = min(n - 1, (PREFILL_PAIRS * t + PREFILL_PAIRS - 1) // G)
+            rows.add(int(qsl[r]) + int(rng.integers(lo, hi + 1)))
+            tiles_covered += 1
+    assert tiles_covered == tiles_launched
     return np.array(sorted(rows), np.int32)
 
 
