@@ -85,8 +85,10 @@ typedef enum pkv_status {
   PKV_ERR_UNSUPPORTED = 2, /* a valid argument this build has no kernel for    */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
   PKV_ERR_LAUNCH = 4,      /* the HIP runtime rejected a kernel launch         */
-  PKV_ERR_DEVICE_DATA = 5  /* checked build only: device data broke a
+  PKV_ERR_DEVICE_DATA = 5, /* checked build only: device data broke a
                               precondition (see pkv_debug_check_flags)        */
+  PKV_ERR_SCRATCH_LIMIT = 6 /* pkv_paged_attention_varlen_noalloc: the sizes
+                              need more than PKV_NOALLOC_SCRATCH_BYTES        */
 } pkv_status;
 
 /*
@@ -449,6 +451,39 @@ pkv_status pkv_paged_attention_run(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     float scale, pkv_dtype dtype, const float* k_scale, const float* v_scale,
     int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attention_varlen_noalloc -- pkv_paged_attention_varlen for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace.  The work list and the split-KV partials live in a static
+ * device array of PKV_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one
+ * per GPU, held from the library's first use on that GPU until the process
+ * ends; the call allocates nothing and calls no allocating routine.  Inputs
+ * and outputs are the caller's, exactly as for pkv_paged_attention_varlen
+ * (same arguments minus workspace / workspace_bytes, same kernels and the
+ * same results).  All calls on one GPU share that GPU's array and leave their
+ * data in it: two calls that overlap in time on one GPU (different streams,
+ * or host threads without ordering) race and their results are unspecified;
+ * calls ordered on one stream are fine.  The array's contents on entry do not
+ * matter (everything a call reads there it wrote first).  The current device
+ * must be the device of `stream`.
+ * Errors: those of pkv_paged_attention_varlen except PKV_ERR_WORKSPACE, and
+ * PKV_ERR_SCRATCH_LIMIT when pkv_paged_attention_workspace_bytes(...) of the
+ * same sizes exceeds PKV_NOALLOC_SCRATCH_BYTES, checked on the host before
+ * any device access.  That need is 16 bytes per work item plus, when decode
+ * contexts are split, 64 * (head_dim + 2) bytes per (request, kv head,
+ * partition) slot (the partition count is that of the longest context).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+pkv_status pkv_paged_attention_varlen_noalloc(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, int32_t split_tokens, void* stream);
 
 /*
  * pkv_copy_blocks -- copy-on-write of whole blocks, both pools at once.

@@ -22,7 +22,9 @@ REGULAR_LIB_PATH = os.path.join(HERE, "libpkv.so")
 CHECKED_LIB_PATH = os.path.join(HERE, "libpkv_checked.so")
 LIB_PATH = CHECKED_LIB_PATH if os.environ.get("PKV_DEBUG_CHECKS") == "1" else REGULAR_LIB_PATH
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE_DATA = range(6)
+(OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_DEVICE_DATA,
+ ERR_SCRATCH_LIMIT) = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 # PKV_CHECK_* bits of the checked build (include/pkv.h)
 CHECK_BITS = {"counts": 0x001, "block_id": 0x002, "slot": 0x004, "slot_dup": 0x008, "qsl": 0x010,
               "lengths": 0x020, "row": 0x040, "pairs": 0x080, "scale": 0x100, "plan": 0x200}
@@ -31,8 +33,8 @@ EXPORTS = ("pkv_status_string", "pkv_debug_checks_enabled", "pkv_debug_check_fla
            "pkv_prepare_inputs", "pkv_prepare_input_ids",
            "pkv_kv_cache_write", "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
            "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8",
-           "pkv_paged_attention_plan", "pkv_paged_attention_run", "pkv_copy_blocks",
-           "pkv_zero_blocks")
+           "pkv_paged_attention_plan", "pkv_paged_attention_run",
+           "pkv_paged_attention_varlen_noalloc", "pkv_copy_blocks", "pkv_zero_blocks")
 
 
 class PkvError(RuntimeError):
@@ -92,6 +94,10 @@ def load() -> ctypes.CDLL:
                                             i32, i32, i32, i32, i32, f32, ctypes.c_int, P, P, i32,
                                             P, sz, P]
     lib.pkv_paged_attention_run.restype = ctypes.c_int
+    lib.pkv_paged_attention_varlen_noalloc.argtypes = [P, i64, P, P, i64, P, i64, P, P, P, i64,
+                                                       i32, i32, i32, i32, i32, i32, i32, i32,
+                                                       f32, ctypes.c_int, i32, P]
+    lib.pkv_paged_attention_varlen_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -374,4 +380,32 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     st = load().pkv_paged_attention_varlen(
         *args_head, _dtype_code(q.dtype), int(split_tokens), ws_ptr, ws_bytes, _stream(q.device))
     _check(st, "pkv_paged_attention_varlen")
+    return out
+
+
+def paged_attention_noalloc(q: torch.Tensor, key_cache: torch.Tensor,
+                            value_cache: torch.Tensor, query_start_loc: torch.Tensor,
+                            seq_lens: torch.Tensor, block_table: torch.Tensor, *,
+                            out: torch.Tensor, max_query_len: int, max_seq_len: int,
+                            scale: float | None = None, split_tokens: int = 0) -> torch.Tensor:
+    """pkv_paged_attention_varlen_noalloc: paged_attention with the library's
+    static scratch in place of a workspace.  ``out`` must be given (nothing
+    is allocated on this path, here or in the library)."""
+    T, Hq, d = q.shape
+    nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    R = int(seq_lens.shape[0])
+    assert q.stride(2) == 1 and q.stride(1) == d and out.shape == q.shape
+    assert key_cache.is_contiguous() and value_cache.is_contiguous()
+    assert block_table.dim() == 2 and block_table.stride(1) == 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = load().pkv_paged_attention_varlen_noalloc(
+        _dev(q, name="q"), q.stride(0), _dev(key_cache, q.dtype, "key_cache"),
+        _dev(value_cache, q.dtype, "value_cache"), nb, _dev(out, q.dtype, "out"), out.stride(0),
+        _dev(query_start_loc, torch.int32, "query_start_loc"),
+        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_table, torch.int32, "block_table"),
+        block_table.stride(0), R, T, int(max_query_len), int(max_seq_len), Hq, Hkv, d, bs,
+        float(scale), _dtype_code(q.dtype), int(split_tokens_or_env(split_tokens)),
+        _stream(q.device))
+    _check(st, "pkv_paged_attention_varlen_noalloc")
     return out

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "pkv_internal.h"
 
 namespace {
@@ -42,6 +44,9 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_DEVICE_DATA: return "device data breaks a precondition (checked build)";
+    case PKV_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the static buffer of "
+             "pkv_paged_attention_varlen_noalloc holds (PKV_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -376,6 +381,68 @@ pkv_status pkv_paged_attention_run(
                         bt_row_stride, num_reqs, num_tokens, max_query_len, max_seq_len,
                         num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, k_scale,
                         v_scale, split_tokens, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// pkv_paged_attention_varlen_noalloc: the workspace is a static device array
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// The attention workspace of the allocation-free entry point: one copy per
+// device, held from module load until the process ends, shared by every call
+// on that device.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress.
+__device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // per device, looked up once
+
+// This device's address of `scratch` (the current device).  Concurrent first
+// calls may each look it up; they store the same address.
+pkv_status scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_LAUNCH;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PKV_ERR_LAUNCH;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_varlen_noalloc(
+    const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,
+    int64_t num_blocks, void* out, int64_t out_row_stride, const int32_t* query_start_loc,
+    const int32_t* seq_lens, const int32_t* block_table, int64_t bt_row_stride,
+    int32_t num_reqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, int32_t split_tokens, void* stream) {
+  // the sizes first: a call the static array cannot hold is rejected before
+  // anything touches the device
+  const size_t need = pkv_paged_attention_workspace_bytes(
+      num_reqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len, max_seq_len,
+      split_tokens, dtype);
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (need > 0 && num_tokens > 0 && num_reqs > 0) {
+    const pkv_status st = scratch_address(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return attention_call(AttnMode::kFused, q, q_row_stride, key_cache, value_cache, num_blocks,
+                        out, out_row_stride, query_start_loc, seq_lens, block_table,
+                        bt_row_stride, num_reqs, num_tokens, max_query_len, max_seq_len,
+                        num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, nullptr,
+                        nullptr, split_tokens, ws, ws ? (size_t)PKV_NOALLOC_SCRATCH_BYTES : 0,
+                        stream);
 }
 
 }  // extern "C"

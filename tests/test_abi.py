@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert binding.status_string(code) != "unknown status"
     assert binding.status_string(99) == "unknown status"
 
@@ -268,3 +268,23 @@ def run(lib, **kw):
     (dict(bs=32), binding.ERR_UNSUPPORTED), (dict(), binding.ERR_WORKSPACE)])
 def test_run_rejects(lib, kw, code):
     assert run(lib, **kw) == code
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """pkv_paged_attention_varlen_noalloc refuses a call whose work list and
+    partials exceed PKV_NOALLOC_SCRATCH_BYTES, before any device access."""
+    R, Hkv, Hq, d, split, L = 64, 8, 32, 128, 32, 65536
+    need = binding.attention_workspace_bytes(R, R, Hq, Hkv, d, 1, L, split)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert "#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert binding.NOALLOC_SCRATCH_BYTES == 64 << 20
+    st = lib.pkv_paged_attention_varlen_noalloc(FAKE, Hq * d, FAKE, FAKE, 1 << 16, FAKE, Hq * d,
+                                                FAKE, FAKE, FAKE, 1 << 12, R, R, 1, L, Hq, Hkv,
+                                                d, 16, 0.088, binding.BF16, split, None)
+    assert st == binding.ERR_SCRATCH_LIMIT
+    # bad host arguments are still reported as such when the sizes fit
+    st = lib.pkv_paged_attention_varlen_noalloc(FAKE, Hq * d, FAKE, FAKE, 1 << 16, FAKE, Hq * d,
+                                                FAKE, FAKE, FAKE, 1 << 12, 4, 4, 1, 100, 6, 4,
+                                                d, 16, 0.088, binding.BF16, 0, None)
+    assert st == binding.ERR_INVALID_ARG
