@@ -75,6 +75,9 @@ def parse():
                         "in both pools of the workload's cache geometry")
     p.add_argument("--blocks", type=int, default=8192,
                    help="blocks per copy_blocks / zero_blocks launch")
+    p.add_argument("--clock-runs", type=int, default=300,
+                   help="attention runs queued back to back while the GPU clocks are read "
+                        "(0: no clock reading)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="instead of the step, time a plain device-to-device copy of this many "
                         "MiB (the known-size kernel that HBM byte counters are scaled by)")
@@ -278,13 +281,42 @@ class ClockReader:
             except Exception:
                 pass
 
-            def read():
+            def valid(x):
+                return isinstance(x, (int, float)) and 0 < x < 0xFFFF
+
+            def from_metrics():
+                # per-XCC current gfx clocks where the metrics table has them
+                mt = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                g = mt.get("current_gfxclks")
+                if isinstance(g, (list, tuple)):
+                    g = [x for x in g if valid(x)]
+                    g = float(np.median(g)) if g else None
+                else:
+                    g = None
+                if g is None:
+                    for key in ("current_gfxclk", "average_gfxclk_frequency"):
+                        if valid(mt.get(key)):
+                            g = float(mt[key])
+                            break
+                m = next((float(mt[k]) for k in ("current_uclk", "average_uclk_frequency")
+                          if valid(mt.get(k))), None)
+                if g is None or m is None:
+                    raise ValueError("no clock in the metrics table")
+                return g, m
+
+            def from_clock_info():
                 g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]
                 m = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"]
                 return float(g), float(m)
-            read()
-            self.source = "amdsmi_get_clock_info (GFX, MEM)"
-            return read
+            try:
+                from_metrics()
+                self.source = ("amdsmi_get_gpu_metrics_info (median of the per-XCC current "
+                               "gfx clocks; current uclk)")
+                return from_metrics
+            except Exception:
+                from_clock_info()
+                self.source = "amdsmi_get_clock_info (GFX, MEM)"
+                return from_clock_info
         except Exception:
             pass
         import glob
@@ -684,21 +716,27 @@ def main():
             torch.cuda.synchronize(dev)
             ms = pct([e[0].elapsed_time(e[1]) for e in sev])
             sr = roofline_of(algorithmic_work(sw), ms["median"])
+            sr["traffic"] = measured_traffic(f"w{args.workload}_{name}_split{args.split_tokens}"
+                                             + ("_fp8" if args.kv_dtype == "fp8" else ""))
             sub_lines[name] = {"rows": sw.num_tokens, "requests": sw.num_reqs,
                                "run_ms": ms, **sr}
             del sb
 
-    # clocks while the attention run executes: 300 runs queued back to back
-    # (no flush), read until the last one ends
+    # clocks while the attention run executes: --clock-runs runs queued back
+    # to back (no flush), read until the last one ends
     done_ev = torch.cuda.Event()
 
     def enqueue():
-        for _ in range(300):
+        for _ in range(args.clock_runs):
             run()
         done_ev.record(stream)
 
-    clocks = clock_reader.under_load(enqueue, done_ev.query)
-    clocks["note"] = "sampled while 300 attention runs of the workload executed back to back"
+    if args.clock_runs > 0:
+        clocks = clock_reader.under_load(enqueue, done_ev.query)
+        clocks["note"] = (f"sampled while {args.clock_runs} attention runs of the workload "
+                          "executed back to back")
+    else:
+        clocks = {"note": "not read (--clock-runs 0)"}
     torch.cuda.synchronize(dev)
 
     graph_ms = None
