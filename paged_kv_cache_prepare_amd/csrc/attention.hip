@@ -38,6 +38,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "pkv_internal.h"
 
@@ -1564,30 +1565,52 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a, int32_t gr
   if (a.k_scale != nullptr) c2 *= *a.k_scale;  // partial maxima are raw FP8 scores
   constexpr int kDimsPerThread = D / 16;
   const int cn = threadIdx.x >> 4;
-  const int cd = (threadIdx.x & 15) * kDimsPerThread;
-  if (cn >= pairs) return;
+  const int sl = threadIdx.x & 15;
+  const int cd = sl * kDimsPerThread;
+  if (cn >= pairs) return;  // the 16 lanes of a column leave together
   const int64_t base = (((int64_t)r * a.num_kv_heads + kvh) * max_splits) * kPairsPerTile + cn;
+  // the largest partition maximum: the column's 16 lanes take every 16th
+  // partition, then combine within their 16-lane segment
   float mmax = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mmax = fmaxf(mmax, ml[2 * (base + s * kPairsPerTile)]);
+  for (int s = sl; s < nsplit; s += 16) mmax = fmaxf(mmax, ml[2 * (base + (int64_t)s * kPairsPerTile)]);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off, 16));
+  // weighted sum over the partitions in ascending order; the loads of a
+  // batch of partitions are all issued before any of them is used
+  constexpr int kV = kDimsPerThread / 4;
   float lsum = 0.f;
   float acc[kDimsPerThread];
 #pragma unroll
   for (int k = 0; k < kDimsPerThread; ++k) acc[k] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t idx = base + s * kPairsPerTile;
-    const float ms = ml[2 * idx];
-    const float f = (ms == -INFINITY) ? 0.f : fast_exp2((ms - mmax) * c2);
-    lsum += f * ml[2 * idx + 1];
-    const float* src = opart + idx * D + cd;
+  auto batch = [&](int s0, auto u_count) {
+    constexpr int U = decltype(u_count)::value;
+    float2 mlv[U];
+    f32x4 v[U][kV];
 #pragma unroll
-    for (int k = 0; k < kDimsPerThread; k += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + k);
-      acc[k] += f * v[0];
-      acc[k + 1] += f * v[1];
-      acc[k + 2] += f * v[2];
-      acc[k + 3] += f * v[3];
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = base + (int64_t)min(s0 + u, nsplit - 1) * kPairsPerTile;
+      mlv[u] = *reinterpret_cast<const float2*>(ml + 2 * idx);
+#pragma unroll
+      for (int k = 0; k < kV; ++k)
+        v[u][k] = *reinterpret_cast<const f32x4*>(opart + idx * D + cd + 4 * k);
     }
-  }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its arithmetic
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = s0 + u < nsplit;  // a select, so the loads above stay hoisted
+      const float ms = mlv[u].x;
+      const float f = (ms == -INFINITY) ? 0.f : fast_exp2((ms - mmax) * c2);
+      lsum = in ? lsum + f * mlv[u].y : lsum;
+#pragma unroll
+      for (int k = 0; k < kV; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[4 * k + i] = in ? acc[4 * k + i] + f * v[u][k][i] : acc[4 * k + i];
+    }
+  };
+  int s0 = 0;
+  for (; s0 + 8 <= nsplit; s0 += 8) batch(s0, std::integral_constant<int, 8>());
+  for (; s0 < nsplit; s0 += 2) batch(s0, std::integral_constant<int, 2>());
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int tt = cn / group;
   const int hh = kvh * group + (cn - tt * group);
