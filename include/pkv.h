@@ -50,7 +50,11 @@
  *   buffers described here; the affected outputs are then unspecified.
  * - Integer index tensors are int32 except slot_mapping (int64, -1 = no
  *   write).  Block pools are two separate tensors:
- *     K pool: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major)
+ *     K pool: [num_blocks][num_kv_heads][head_dim * block_size], each
+ *             (block, head) run in slabs of 32 dims: element (dim, t) at
+ *             ((dim / 32) * block_size + t) * 32 + dim % 32 (when 32 does
+ *             not divide head_dim the slab spans all dims: then the run is
+ *             plain [block_size][head_dim])
  *     V pool: [num_blocks][num_kv_heads][head_dim * block_size], each
  *             (block, head) run in tiles of 16 dims x 4 tokens:
  *             element (dim, t) at ((dim / 16) * (block_size / 4) + t / 4) * 64
@@ -59,11 +63,16 @@
  *             tokens: then the run is plain [head_dim][block_size])
  *   The pages leave the cache layout to the kernel ("Inside vLLM: Following
  *   One Request from the API to GPU Execution", Part 5, which notes that
- *   different write/read kernel pairs use different layouts).  In a V tile
- *   the 4 tokens of one dimension are one contiguous run, the operand unit
- *   of the P.V contraction over tokens, and a single token's row of 128
- *   16-bit values spans 8 cache lines of 128 bytes per head (a dim-major
- *   run would spread it over 32, each partly written).
+ *   different write/read kernel pairs use different layouts).  A K slab of
+ *   a 16-token block is 1 KB (16-bit elements) holding, for each token, 32
+ *   contiguous dims: one wave-wide 16-byte load reads a whole slab, the
+ *   operand of one 32-deep step of the Q.K contraction, as 8 full cache
+ *   lines (token-major rows would take 16 half lines), and a token's row of
+ *   128 16-bit values spans 4 runs of 64 bytes.  In a V tile the 4 tokens
+ *   of one dimension are one contiguous run, the operand unit of the P.V
+ *   contraction over tokens, and a single token's row of 128 16-bit values
+ *   spans 8 cache lines of 128 bytes per head (a dim-major run would spread
+ *   it over 32, each partly written).
  * - Ordering: the KV write of a step must be enqueued before the attention
  *   that reads it, on the same stream or behind an event.  The pages make the
  *   same requirement explicit with a dummy data dependency ("Inside vLLM...",
@@ -227,7 +236,8 @@ pkv_status pkv_prepare_input_ids(const int32_t* token_table, int64_t row_width,
  * slot_mapping[i] = physical_block * block_size + in_block_offset; the write
  * is token-granular while reads are block-granular.  For every i with
  * s = slot_mapping[i] in [0, num_blocks * block_size) and every kv head h:
- *   K pool[s / block_size][h][s % block_size][:] = key[i][h][:]
+ *   K pool element (dim, s % block_size) of run (s / block_size, h)
+ *     = key[i][h][dim] for every dim (slab order above)
  *   V pool element (dim, s % block_size) of run (s / block_size, h)
  *     = value[i][h][dim] for every dim (tiled order above)
  * Bytes are copied unchanged.  Slots < 0 (padding rows) and slots past the
@@ -273,7 +283,9 @@ pkv_status pkv_kv_cache_write(const void* key, const void* value, int64_t key_ro
  * reads back as its E4M3 value times the scale.
  *
  * FP8 pool layouts (bytes; block_size 16, head_dim a multiple of 64):
- *   K pool: [num_blocks][num_kv_heads][16][head_dim]            (token-major)
+ *   K pool: [num_blocks][num_kv_heads][head_dim * 16], each (block, head) run
+ *           ordered [dim / 64][token][dim % 64]: slabs of 64 dims, 1 KB each,
+ *           one 16-byte load of the attention kernels per slab and lane
  *   V pool: [num_blocks][num_kv_heads][head_dim * 16], each (block, head) run
  *           ordered [dim / 64][token / 4][dim % 16][(dim / 16) % 4][token % 4],
  *           so 16 consecutive bytes hold 4 tokens of 4 dims 16 apart -- one

@@ -203,8 +203,9 @@ def kv_write(key, value, key_cache, value_cache, slot_mapping, block_size: int) 
     """Scatter new K/V rows into the caches in place; see ``orc_kv_write``.
 
     ``key``/``value`` are [T, Hkv, d] CPU tensors or arrays (any 2- or 4-byte
-    dtype; bytes are copied unchanged).  ``key_cache`` is [nb, Hkv, bs, d],
-    ``value_cache`` holds nb * Hkv runs of d * bs elements, each in
+    dtype; bytes are copied unchanged).  Both caches hold nb * Hkv runs of
+    d * bs elements ([nb, Hkv, d * bs]): a K run in slabs of 32 dims
+    ([d / 32][bs][32], plain [bs][d] when 32 does not divide d), a V run in
     tiles of 16 dims x 4 tokens ([d / 16][bs / 4][16][4], plain [d][bs] when
     16 does not divide d or 4 does not divide bs).
     """
@@ -234,8 +235,9 @@ def kv_write_fp8(key, value, key_cache, value_cache, slot_mapping, block_size: i
     """FP8 form of :func:`kv_write`; see ``orc_kv_write_fp8``.
 
     ``key``/``value`` are [T, Hkv, d] bf16 or fp32; the pools are uint8 arrays or
-    tensors with [nb, Hkv, bs, d] (K) and [nb, Hkv, d * bs] (V, the FP8 layout)
-    bytes; the scales are binary32 values.
+    tensors of [nb, Hkv, d * bs] bytes in the FP8 layouts (K runs
+    [d / 64][bs][64], V runs as in ``orc_v8_byte``); the scales are binary32
+    values.
     """
     T, H, d = key.shape
     nb = key_cache.shape[0]

@@ -42,10 +42,11 @@
  *                     kv_cache_dtype, k_scale and v_scale).
  *
  * Cache layout (an interface fact, not part of the method; the pages leave the
- * layout open): K pool [num_blocks][num_kv_heads][block_size][head_dim],
- * row-major; each (block, head) run of the 16-bit and fp32 V pool holds
- * tiles of 16 dims x 4 tokens, [dim / 16][token / 4][dim % 16][token % 4]
- * (see orc_v_elem).
+ * layout open): both pools are [num_blocks][num_kv_heads][run], one run of
+ * head_dim x block_size elements per (block, head).  A 16-bit or fp32 K run
+ * is [dim / 32][token][dim % 32] (slabs of 32 dims, see orc_k_elem); a V run
+ * holds tiles of 16 dims x 4 tokens, [dim / 16][token / 4][dim % 16]
+ * [token % 4] (see orc_v_elem).
  *
  * Readings of points the pages leave open (each also listed in the design
  * notes of the repository):
@@ -216,9 +217,16 @@ int orc_zero_blocks(uint8_t* key_cache, uint8_t* value_cache, int64_t num_blocks
 /* kv_write                                                                  */
 /* ------------------------------------------------------------------------ */
 
+/* Element of (block, head, token, dim) in a 16-bit or fp32 K pool.  Each
+ * (block, head) run of head_dim * block_size elements is cut into slabs of
+ * KW dims, ordered [dim / KW][token][dim % KW], with KW = 32 -- or KW =
+ * head_dim when 32 does not divide it (then the run is plain [token][dim]).
+ * An interface fact of the library's pools. */
 static int64_t orc_k_elem(int64_t block, int32_t head, int32_t tok, int32_t dim,
                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim) {
-  return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;
+  const int32_t kw = head_dim % 32 == 0 ? 32 : head_dim;
+  const int64_t run = (block * num_kv_heads + head) * (int64_t)head_dim * block_size;
+  return run + ((int64_t)(dim / kw) * block_size + tok) * kw + dim % kw;
 }
 
 /* Element of (block, head, token, dim) in a 16-bit or fp32 V pool.  Each
@@ -346,11 +354,14 @@ uint8_t orc_fp8_encode(float x) {
   return sign | (uint8_t)(((e + 7) << 3) | m);
 }
 
-/* Byte of (block, head, token, dim) in an FP8 K pool: token-major like the
- * 16-bit pools, [num_blocks][num_kv_heads][block_size][head_dim]. */
+/* Byte of (block, head, token, dim) in an FP8 K pool (block_size 16, head_dim
+ * a multiple of 64).  Each (block, head) run of head_dim * 16 bytes is laid
+ * out as [dim / 64][token][dim % 64]: slabs of 64 dims, one 64-byte row per
+ * token.  An interface fact of the library's pools. */
 static int64_t orc_k8_byte(int64_t block, int32_t head, int32_t tok, int32_t dim,
                            int32_t num_kv_heads, int32_t block_size, int32_t head_dim) {
-  return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;
+  const int64_t run = (block * num_kv_heads + head) * (int64_t)head_dim * block_size;
+  return run + ((int64_t)(dim / 64) * block_size + tok) * 64 + dim % 64;
 }
 
 /* Byte of (block, head, token, dim) in an FP8 V pool (block_size 16, head_dim

@@ -232,6 +232,14 @@ def paged_attention_plan(query_start_loc: torch.Tensor, seq_lens: torch.Tensor, 
     return workspace
 
 
+def _pool_block_size(key_cache: torch.Tensor, value_cache: torch.Tensor, head_dim: int) -> int:
+    """Tokens per block of [nb, Hkv, head_dim * block_size] pools."""
+    assert key_cache.dim() == 3 and value_cache.shape == key_cache.shape, \
+        "pools are [num_blocks, num_kv_heads, head_dim * block_size]"
+    assert key_cache.shape[2] % head_dim == 0
+    return key_cache.shape[2] // head_dim
+
+
 def _pool_block_bytes(key_cache: torch.Tensor, value_cache: torch.Tensor) -> int:
     assert key_cache.is_contiguous() and value_cache.is_contiguous()
     assert key_cache.shape[0] == value_cache.shape[0] and key_cache.dtype == value_cache.dtype
@@ -269,7 +277,8 @@ def zero_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
 def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                    value_cache: torch.Tensor, slot_mapping: torch.Tensor, *,
                    block_size: int) -> None:
-    """pkv_kv_cache_write.  key/value: [T, Hkv, d] with contiguous rows."""
+    """pkv_kv_cache_write.  key/value: [T, Hkv, d] with contiguous rows; pools
+    [nb, Hkv, d * block_size] (workloads.key_pool / value_pool order)."""
     T, H, d = key.shape
     for t in (key, value):
         assert t.stride(2) == 1 and t.stride(1) == d, "heads and dims must be contiguous"
@@ -286,8 +295,8 @@ def kv_cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.
                        value_cache: torch.Tensor, slot_mapping: torch.Tensor,
                        k_scale: torch.Tensor, v_scale: torch.Tensor, *, block_size: int) -> None:
     """pkv_kv_cache_write_fp8.  key/value: [T, Hkv, d] (bf16 or fp32) with
-    contiguous rows; pools are uint8 tensors in the FP8 layouts (K [nb, Hkv,
-    16, d], V [nb, Hkv, d * 16]); scales are one-element float32 device tensors."""
+    contiguous rows; pools are uint8 tensors [nb, Hkv, d * 16] in the FP8
+    layouts; scales are one-element float32 device tensors."""
     T, H, d = key.shape
     for t in (key, value):
         assert t.stride(2) == 1 and t.stride(1) == d, "heads and dims must be contiguous"
@@ -329,13 +338,15 @@ def paged_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                     k_scale: torch.Tensor | None = None,
                     v_scale: torch.Tensor | None = None, planned: bool = False) -> torch.Tensor:
     """pkv_paged_attention_varlen (or _fp8 when k_scale / v_scale are given).
-    q: [T, Hq, d]; 16-bit pools: K [nb, Hkv, 16, d], V [nb, Hkv, d * 16] in
-    tiles of 16 dims x 4 tokens (workloads.value_pool); FP8 pools (uint8):
-    K [nb, Hkv, 16, d], V [nb, Hkv, d * 16]; scales: one-element float32
-    device tensors.  planned=True: pkv_paged_attention_run over the work
-    list a paged_attention_plan call left in ``workspace``."""
+    q: [T, Hq, d]; 16-bit pools: K [nb, Hkv, d * 16] in slabs of 32 dims
+    (workloads.key_pool), V [nb, Hkv, d * 16] in tiles of 16 dims x 4 tokens
+    (workloads.value_pool); FP8 pools (uint8): K and V [nb, Hkv, d * 16] in
+    the FP8 layouts; scales: one-element float32 device tensors.
+    planned=True: pkv_paged_attention_run over the work list a
+    paged_attention_plan call left in ``workspace``."""
     T, Hq, d = q.shape
-    nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    nb, Hkv = key_cache.shape[0], key_cache.shape[1]
+    bs = _pool_block_size(key_cache, value_cache, d)
     split_tokens = split_tokens_or_env(split_tokens)
     fp8 = k_scale is not None
     if fp8:
@@ -392,7 +403,8 @@ def paged_attention_noalloc(q: torch.Tensor, key_cache: torch.Tensor,
     static scratch in place of a workspace.  ``out`` must be given (nothing
     is allocated on this path, here or in the library)."""
     T, Hq, d = q.shape
-    nb, Hkv, bs = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+    nb, Hkv = key_cache.shape[0], key_cache.shape[1]
+    bs = _pool_block_size(key_cache, value_cache, d)
     R = int(seq_lens.shape[0])
     assert q.stride(2) == 1 and q.stride(1) == d and out.shape == q.shape
     assert key_cache.is_contiguous() and value_cache.is_contiguous()

@@ -493,8 +493,8 @@ __device__ inline void issue_step_loads(StepLoads<D>& ld, const StepRsrc& r, int
                                         int v_lane) {
 #pragma unroll
   for (int s = 0; s < Geometry<D>::KS; ++s) {
-    ld.k0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + s * 64, 0, kKvLoadPolicy));
-    ld.k1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + s * 64, 0, kKvLoadPolicy));
+    ld.k0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + s * 1024, 0, kKvLoadPolicy));
+    ld.k1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + s * 1024, 0, kKvLoadPolicy));
   }
 #pragma unroll
   for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
@@ -623,7 +623,9 @@ __device__ __attribute__((always_inline)) inline void walk_steps(
   if (s_begin >= s_end) return;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
-  const int k_lane = (n * D + 8 * g) * 2;
+  // K slab s of a run (1 KB): token n, dims 32s + 8g .. + 7 at 64 n + 16 g;
+  // the 64 lanes of one load read the whole slab
+  const int k_lane = 64 * n + 16 * g;
   const int v_lane = 128 * g + 8 * n;
   const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
   const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
@@ -678,11 +680,12 @@ __device__ __attribute__((always_inline)) inline void walk_steps(
 // FP8 E4M3 pools: the decode walk
 // ---------------------------------------------------------------------------
 //
-// An FP8 run of one (block, kv head) is 16 * D bytes.  K is token-major; a
-// lane's 16-byte load of token n at dims 64t + 16g .. + 15 holds the A
-// operands of QK k-steps 2t (its first 8 bytes) and 2t + 1 (the last 8): the
-// contraction over dims may run in any order as long as Q follows the same
-// one.  V runs are laid out [dim / 64][token / 4][dim % 16][(dim / 16) % 4]
+// An FP8 run of one (block, kv head) is 16 * D bytes.  K runs are slabs of
+// 64 dims, [dim / 64][token][dim % 64]; the 16-byte load of lane (n, g) in
+// slab t is token n, dims 64t + 16g .. + 15 (one load instruction reads the
+// whole 1 KB slab), and holds the A operands of QK k-steps 2t (its first 8
+// bytes) and 2t + 1 (the last 8): the contraction over dims may run in any
+// order as long as Q follows the same one.  V runs are laid out [dim / 64][token / 4][dim % 16][(dim / 16) % 4]
 // [token % 4], so one 16-byte load of lane (n, g) holds tokens 4g..4g+3 of
 // dims 64 dq + 16 dt + n for four 16-dim tiles dt: the V^T operand runs of
 // four PV MFMAs.  Codes widen exactly to bf16; k_scale is folded into the
@@ -739,8 +742,8 @@ __device__ inline void issue_step_loads8(StepLoads8<D>& ld, const StepRsrc& r, i
                                          int v_lane) {
 #pragma unroll
   for (int t = 0; t < Geometry8<D>::KL; ++t) {
-    ld.k0[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + 64 * t, 0, kKvLoadPolicy);
-    ld.k1[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + 64 * t, 0, kKvLoadPolicy);
+    ld.k0[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + 1024 * t, 0, kKvLoadPolicy);
+    ld.k1[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + 1024 * t, 0, kKvLoadPolicy);
   }
 #pragma unroll
   for (int q = 0; q < Geometry8<D>::VL; ++q) {
@@ -820,7 +823,7 @@ __device__ __attribute__((always_inline)) inline void walk_steps8(
   if (s_begin >= s_end) return;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
-  const int k_lane = n * D + 16 * g;
+  const int k_lane = 64 * n + 16 * g;  // + 1024 t: token n, dims 64t + 16g .. + 15
   const int v_lane = (16 * g + n) * 16;
   const int lim = min(nblk, (int)min<int64_t>(a.bt_stride, 0x7fffffff));
   const int last_col = (int)min<int64_t>(a.bt_stride, 0x7fffffff) - 1;
@@ -1308,9 +1311,11 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
   //          dims 16 dt + 2p and +1 of tokens 4u..4u+3.  A PV operand (8
   //          tokens of one dim) is two 8-byte reads of token groups 2c and
   //          2c+1, 128 bytes apart.
-  // Source offsets of copy q: K token (lane & 15), dims 8(4q + (lane >> 4));
-  // V slot q * 64 + lane.  Both are a lane base plus q times a constant.
-  const int k_src = (lane & 15) * 2 * D + 16 * (lane >> 4);            // + 64 q
+  // Source offsets of copy q: K token (lane & 15), dims 8(4q + (lane >> 4)),
+  // which in the pool's 32-dim slabs is slab q at 64 (lane & 15) + 16 (lane
+  // >> 4): each copy reads one whole 1 KB slab; V slot q * 64 + lane.  Both
+  // are a lane base plus q times a constant.
+  const int k_src = 64 * (lane & 15) + 16 * (lane >> 4);              // + 1024 q
   const int v_u = (lane >> 3) & 3;  // token group of this lane's V slots
   const int v_src = 16 * lane;      // + 1024 q
   typedef __attribute__((address_space(3))) void lds_void;
@@ -1353,7 +1358,7 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
 #pragma unroll
       for (int q = 0; q < KQ; ++q) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk_d, (lds_void*)(kdst + q * 1024), 16,
-                                                 k_src + 64 * q, 0, 0, kPrefillLoadPolicy);
+                                                 k_src + 1024 * q, 0, 0, kPrefillLoadPolicy);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv_d, (lds_void*)(vdst + q * 1024), 16,
                                                  v_src + 1024 * q, 0, 0, kPrefillLoadPolicy);
       }
@@ -1373,9 +1378,10 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
 #pragma unroll
       for (int q = 0; q < KQ; ++q) {
         if (!ok) break;
-        // K: token lane & 15, dims 8(4q + (lane >> 4)) .. + 7
+        // K: token lane & 15, dims 8(4q + (lane >> 4)) .. + 7, in 64-dim
+        // slab q / 2 at byte 32 (q % 2) + 8 (lane >> 4) of the token's row
         const u32x2 k8 = *reinterpret_cast<const u32x2*>(
-            stage_k + (lane & 15) * D + 8 * (4 * q + (lane >> 4)));
+            stage_k + (q >> 1) * 1024 + (lane & 15) * 64 + 32 * (q & 1) + 8 * (lane >> 4));
         *reinterpret_cast<u32x4*>(kdst + q * 1024 + 16 * lane) =
             __builtin_bit_cast(u32x4, fp8x8_to_bf16(k8.x, k8.y));
       }
@@ -1634,6 +1640,12 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a, int32_t gr
 // fp32 path: one wave per (row, q head)
 // ---------------------------------------------------------------------------
 
+// Element of (dim, token) in a (block, kv head) K run: slabs of 32 dims,
+// [dim / 32][token][dim % 32].
+__device__ inline int k_slab_elem(int dim, int tok) {
+  return ((dim >> 5) * kBlock + tok) * 32 + (dim & 31);
+}
+
 // Element of (dim, token) in a (block, kv head) V run: tiles of 16 dims x 4
 // tokens, [dim / 16][token / 4][dim % 16][token % 4].
 __device__ inline int v_tile_elem(int dim, int tok) {
@@ -1684,7 +1696,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int32_t group)
     const int64_t head_base = (int64_t)phys * a.num_kv_heads + kvh;
     float dot = 0.f;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) dot += qv[k] * kc[(head_base * kBlock + off) * D + lane + 64 * k];
+    for (int k = 0; k < PER; ++k)
+      dot += qv[k] * kc[head_base * D * kBlock + k_slab_elem(lane + 64 * k, off)];
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh, 64);
     const float s = dot * a.scale;

@@ -5,8 +5,10 @@
 // slot_mapping[i] = block * block_size + offset.  HBM-bound copy; no math.
 //
 // One workgroup handles 16 consecutive tokens of one kv head.
-//  * K pool rows [block][head][offset][:] are contiguous per token, so each
-//    thread moves one 16-byte chunk (global load -> global store).
+//  * K runs ([block][head] runs of head_dim x block_size) are slabs of 32
+//    dims, [dim / 32][offset][dim % 32] (k_elem): each thread moves one
+//    16-byte chunk of a token's row (global load -> global store), which
+//    lands inside one slab row.
 //  * V runs ([block][head] runs of head_dim x 16) are tiles of 16 dims x 4
 //    offsets (v_elem), so that a decode token's row touches 8 cache lines
 //    per head (head_dim 128) rather than 32: each partly written line costs
@@ -27,6 +29,16 @@ constexpr int kTileTokens = 16;
 constexpr int kMaxRowBytes = 1024;  // head_dim * element bytes
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Element of (dim, offset) inside one (block, head) K run of head_dim x
+// block_size elements: slabs of KW dims ordered [dim / KW][offset][dim % KW],
+// KW = 32 (KW = head_dim when 32 does not divide it).  One 32-dim slab of a
+// 16-token block is what a wave-wide 16-byte load of the attention kernels
+// reads at once.
+__device__ inline int64_t k_elem(int dim, int off, int head_dim, int block_size) {
+  const int kw = head_dim % 32 == 0 ? 32 : head_dim;
+  return ((int64_t)(dim / kw) * block_size + off) * kw + dim % kw;
+}
 
 // Element of (dim, offset) inside one (block, head) V run of head_dim x
 // block_size elements: tiles of DW dims x TG offsets ordered
@@ -79,9 +91,11 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
       vv = *reinterpret_cast<const u32x4*>(
           value + (row * value_stride + (int64_t)h * head_dim) * E + c * 16);
       const int64_t blk = s / block_size;
-      const int64_t off = s - blk * block_size;
+      const int off = (int)(s - blk * block_size);
+      const int64_t run = (int64_t)head_dim * block_size;  // elements of one (block, head) run
       __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(
-          key_cache + (((blk * num_kv_heads + h) * block_size + off) * head_dim) * E + c * 16));
+          key_cache + ((blk * num_kv_heads + h) * run +
+                       k_elem(c * (16 / E), off, head_dim, block_size)) * E));
     }
     s_v[tk * chunks + c] = vv;
   }
@@ -148,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
 // the write call's kv_cache_dtype, k_scale and v_scale): each element is
 // stored as the E4M3 code of value / scale (binary32 division, nearest with
 // ties to even; finite magnitudes beyond 448 saturate).
-//  * K pool: [block][head][offset][dim] bytes, one 16-byte store per 16 dims.
+//  * K pool: each (block, head) run of head_dim * 16 bytes is
+//    [dim / 64][offset][dim % 64], one 16-byte store per 16 dims.
 //  * V pool: each (block, head) run of head_dim * 16 bytes is
 //    [dim / 64][offset / 4][dim % 16][(dim / 16) % 4][offset % 4]: 16
 //    consecutive bytes are 4 tokens of 4 dims 16 apart, the unit the
@@ -229,7 +244,8 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
     const int64_t off = s - blk * kTileTokens;
     __builtin_nontemporal_store(u32x4{kw[0], kw[1], kw[2], kw[3]},
                                 reinterpret_cast<u32x4*>(key_cache + (blk * num_kv_heads + h) * run +
-                                                         off * head_dim + 16 * c));
+                                                         ((c >> 2) * kTileTokens + off) * 64 +
+                                                         16 * (c & 3)));
     *reinterpret_cast<u32x4*>(&s_v[tk][16 * c]) = u32x4{vw[0], vw[1], vw[2], vw[3]};
   }
   __syncthreads();

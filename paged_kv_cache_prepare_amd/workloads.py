@@ -22,14 +22,15 @@ Recipe (every configuration):
   lets a masked value into a sum, produces NaN.
 
 Layouts (the library's interface, not part of the method): new rows are
-[T, H, d]; the K pool is [num_blocks, Hkv, block_size, d]; the V pool is
-[num_blocks, Hkv, d, block_size].
+[T, H, d]; the pools are [num_blocks, Hkv, d * block_size], the K pool in
+slabs of 32 dims per (block, head) run (``key_pool``), the V pool in tiles of
+16 dims x 4 tokens (``value_pool``).
 
 FP8 pools (``to_fp8``): the same history as E4M3 codes of value / scale,
 converted by torch's float8_e4m3fn (after clamping to +-448; NaN poison stays
-NaN), as uint8 tensors: K [num_blocks, Hkv, 16, d] token-major, V
-[num_blocks, Hkv, d * 16] in the documented FP8 V order (per run: dim / 64,
-token / 4, dim % 16, (dim / 16) % 4, token % 4).
+NaN), as uint8 tensors [num_blocks, Hkv, d * 16]: K in slabs of 64 dims (per
+run: dim / 64, token, dim % 64), V in the documented FP8 V order (per run:
+dim / 64, token / 4, dim % 16, (dim / 16) % 4, token % 4).
 
 The five named configurations are the shapes of the pages' workloads: a
 three-request step of the worked example ("Building the Batch", "How they are
@@ -66,7 +67,7 @@ class Workload:
     q: torch.Tensor = None             # [T, Hq, d]
     key: torch.Tensor = None           # [T, Hkv, d]
     value: torch.Tensor = None         # [T, Hkv, d]
-    key_cache: torch.Tensor = None     # [nb, Hkv, bs, d]
+    key_cache: torch.Tensor = None     # [nb, Hkv, d * bs] (key_pool order), or FP8 codes
     value_cache: torch.Tensor = None   # [nb, Hkv, d * bs] (value_pool order), or FP8 codes
     notes: dict = field(default_factory=dict)
     kv_scales: tuple = None            # (k_scale, v_scale) when the pools hold FP8 codes
@@ -185,6 +186,7 @@ def build(name: str, nst, nct, *, num_q_heads: int, num_kv_heads: int, head_dim:
     hist = torch.from_numpy(history).to(device)
     kc.masked_fill_(~hist[:, None, :, None], float("nan"))
     vc.masked_fill_(~hist[:, None, None, :], float("nan"))
+    kc = key_pool(kc)
     vc = value_pool(vc)
     q = _randn(gen, (T, H, d), dtype, device)
     k_new = _randn(gen, (T, Hkv, d), dtype, device)
@@ -198,6 +200,38 @@ def build(name: str, nst, nct, *, num_q_heads: int, num_kv_heads: int, head_dim:
     wl.notes["shared_blocks"] = n_shared_blocks
     wl.notes["unique_blocks"] = unique_need
     return wl
+
+
+def _key_slab(head_dim: int) -> int:
+    return 32 if head_dim % 32 == 0 else head_dim
+
+
+def key_pool(logical: torch.Tensor) -> torch.Tensor:
+    """A 16-bit or fp32 K pool from its logical form [nb, Hkv, bs, d] (element
+    [b, h, tok, dim]): [nb, Hkv, d * bs], each (block, head) run in slabs of
+    32 dims, [dim / 32][tok][dim % 32] (plain [tok][dim] when 32 does not
+    divide d)."""
+    nb, H, bs, d = logical.shape
+    kw = _key_slab(d)
+    x = logical.reshape(nb, H, bs, d // kw, kw).transpose(2, 3)
+    return x.reshape(nb, H, d * bs).contiguous()
+
+
+def key_logical(pool: torch.Tensor, head_dim: int, block_size: int) -> torch.Tensor:
+    """The inverse of key_pool: [nb, Hkv, bs, d] from a K pool."""
+    nb, H = pool.shape[0], pool.shape[1]
+    kw = _key_slab(head_dim)
+    x = pool.reshape(nb, H, head_dim // kw, block_size, kw).transpose(2, 3)
+    return x.reshape(nb, H, block_size, head_dim).contiguous()
+
+
+def fp8_key_pool(logical: torch.Tensor) -> torch.Tensor:
+    """An FP8 K pool from logical codes [nb, Hkv, 16, d] (d a multiple of 64):
+    [nb, Hkv, d * 16], each run in slabs of 64 dims, [dim / 64][tok][dim % 64]."""
+    nb, H, bs, d = logical.shape
+    assert bs == 16 and d % 64 == 0
+    x = logical.reshape(nb, H, bs, d // 64, 64).transpose(2, 3)
+    return x.reshape(nb, H, d * bs).contiguous()
 
 
 def _value_tiles(head_dim: int, block_size: int) -> tuple[int, int]:
@@ -241,12 +275,13 @@ def to_fp8(wl: Workload, k_scale: float, v_scale: float) -> Workload:
     """The same step with FP8 pools: every history element as the E4M3 code of
     value / scale (torch's float8_e4m3fn conversion).  New rows stay bf16."""
     assert wl.dtype == torch.bfloat16
-    nb, H, bs, d = wl.key_cache.shape
+    nb, H = wl.key_cache.shape[0], wl.key_cache.shape[1]
+    bs, d = wl.block_size, wl.head_dim
 
     def codes(x, scale):
         return (x.float() / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
 
-    kc = codes(wl.key_cache, k_scale).contiguous()
+    kc = fp8_key_pool(codes(key_logical(wl.key_cache, d, bs), k_scale))
     order = torch.from_numpy(fp8_value_order(d, bs)).to(wl.value_cache.device)
     logical_v = value_logical(wl.value_cache, d, bs)
     vc = codes(logical_v, v_scale).reshape(nb, H, d * bs)[:, :, order].contiguous()

@@ -124,8 +124,8 @@ def _kv_case(T, H, d, bs, nb, dtype, seed, consecutive):
     rng = np.random.default_rng(seed)
     key = torch.randn(T, H, d, generator=g).to(dtype)
     val = torch.randn(T, H, d, generator=g).to(dtype)
-    kc = torch.randn(nb, H, bs, d, generator=g).to(dtype)
-    vc = torch.randn(nb, H, d, bs, generator=g).to(dtype)
+    kc = torch.randn(nb, H, d * bs, generator=g).to(dtype)
+    vc = torch.randn(nb, H, d * bs, generator=g).to(dtype)
     if consecutive:  # a prompt chunk: runs of consecutive slots, some not block aligned
         start = int(rng.integers(0, nb * bs - T))
         slots = np.arange(start, start + T, dtype=np.int64)
@@ -166,8 +166,8 @@ def test_kv_write_strided_rows():
     qkv = torch.randn(T, (Hq + 2 * H) * d, generator=g).to(torch.bfloat16)
     key = qkv[:, Hq * d:(Hq + H) * d].view(T, H, d)
     val = qkv[:, (Hq + H) * d:].view(T, H, d)
-    kc = torch.zeros(nb, H, bs, d, dtype=torch.bfloat16)
-    vc = torch.zeros(nb, H, d, bs, dtype=torch.bfloat16)
+    kc = torch.zeros(nb, H, d * bs, dtype=torch.bfloat16)
+    vc = torch.zeros(nb, H, d * bs, dtype=torch.bfloat16)
     slots = np.random.default_rng(4).permutation(nb * bs)[:T].astype(np.int64)
     okc, ovc = kc.clone(), vc.clone()
     oracle.kv_write(key.contiguous(), val.contiguous(), okc, ovc, slots, bs)
@@ -226,13 +226,15 @@ def test_kv_write_fp8_rounding_matches_oracle():
     val = key.clone()
     dev = device()
     nb = -(-T // 16)
-    kc = torch.zeros(nb, 1, 16, d, dtype=torch.uint8, device=dev)
+    kc = torch.zeros(nb, 1, d * 16, dtype=torch.uint8, device=dev)
     vc = torch.zeros(nb, 1, d * 16, dtype=torch.uint8, device=dev)
     ks, vs = _fp8_scales(dev, 1.0, 1.0)
     pkv.kv_cache_write_fp8(key.to(dev), val.to(dev), kc, vc, torch.arange(T, device=dev), ks, vs,
                            block_size=16)
     torch.cuda.synchronize()
-    got = kc.cpu().numpy().reshape(-1)[:len(vals)]
+    # K runs are [dim / 64][token][dim % 64]: back to token-major order
+    got = kc.cpu().reshape(nb, 1, d // 64, 16, 64).permute(0, 1, 3, 2, 4).reshape(-1).numpy()
+    got = got[:len(vals)]
     want = np.array([oracle.fp8_encode(v) for v in vals], np.uint8)
     bad = np.nonzero(got != want)[0]
     assert len(bad) == 0, [(float(vals[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
@@ -246,7 +248,7 @@ def test_kv_write_fp8_vs_oracle(dtype, d, consecutive):
     key, val, _, _, slots = _kv_case(T, H, d, bs, nb, dtype, 11 + d, consecutive)
     key, val = key * 3, val * 0.5
     g = torch.Generator().manual_seed(d)
-    kc = torch.randint(0, 256, (nb, H, bs, d), generator=g, dtype=torch.uint8)
+    kc = torch.randint(0, 256, (nb, H, d * bs), generator=g, dtype=torch.uint8)
     vc = torch.randint(0, 256, (nb, H, d * bs), generator=g, dtype=torch.uint8)
     okc, ovc = kc.clone(), vc.clone()
     oslots = slots.copy()

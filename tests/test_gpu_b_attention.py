@@ -299,11 +299,12 @@ def _shape_scores(wl, growth, seed):
     g = torch.Generator().manual_seed(seed)
     H, d, G = wl.num_kv_heads, wl.head_dim, wl.num_q_heads // wl.num_kv_heads
     u = torch.where(torch.rand(H, d, generator=g) < 0.5, -1.0, 1.0)
-    kc = wl.key_cache.float().cpu()
+    kc = workloads.key_logical(wl.key_cache.float().cpu(), d, 16)
     for r, f in enumerate(growth):
         for p in range(int(wl.num_computed_tokens[r])):
             b, off = int(wl.block_table[r, p // 16]), p % 16
             kc[b, :, off, :] = f(p) * u + 0.5 * torch.randn(H, d, generator=g)
+    kc = workloads.key_pool(kc)
     key = wl.key.float().cpu()
     qsl = np.concatenate([[0], np.cumsum(wl.num_scheduled_tokens)])
     for r, f in enumerate(growth):

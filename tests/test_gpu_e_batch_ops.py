@@ -147,11 +147,11 @@ POOLS = [  # (num_blocks, Hkv, d, dtype): block sizes below, at and above one 16
 def _pools(nb, H, d, dtype, seed, bs=16):
     g = torch.Generator().manual_seed(seed)
     if dtype == "fp8":
-        kc = torch.randint(0, 256, (nb, H, bs, d), generator=g, dtype=torch.uint8)
+        kc = torch.randint(0, 256, (nb, H, d * bs), generator=g, dtype=torch.uint8)
         vc = torch.randint(0, 256, (nb, H, d * bs), generator=g, dtype=torch.uint8)
     else:
-        kc = torch.randn(nb, H, bs, d, generator=g).to(dtype)
-        vc = torch.randn(nb, H, d, bs, generator=g).to(dtype)
+        kc = torch.randn(nb, H, d * bs, generator=g).to(dtype)
+        vc = torch.randn(nb, H, d * bs, generator=g).to(dtype)
     return kc, vc
 
 

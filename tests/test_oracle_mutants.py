@@ -68,8 +68,19 @@ MUTANTS = {
     "fp8 value dim and token fields swapped": ("* 4 + (dim / 16) % 4) * 4 + tok % 4;",
                                                "* 4 + tok % 4) * 4 + (dim / 16) % 4;"),
     "fp8 key stored dim-major": (
-        "int32_t head_dim) {\n  return ((block * num_kv_heads + head) * block_size + tok) * (int64_t)head_dim + dim;\n}\n\n/* Byte of (block, head, token, dim) in an FP8 V pool",
-        "int32_t head_dim) {\n  return ((block * num_kv_heads + head) * head_dim + dim) * (int64_t)block_size + tok;\n}\n\n/* Byte of (block, head, token, dim) in an FP8 V pool"),
+        "return run + ((int64_t)(dim / 64) * block_size + tok) * 64 + dim % 64;",
+        "return run + (int64_t)dim * block_size + tok;"),
+    "fp8 key stored token-major": (
+        "return run + ((int64_t)(dim / 64) * block_size + tok) * 64 + dim % 64;",
+        "return run + (int64_t)tok * head_dim + dim;"),
+    "key stored token-major": (
+        "return run + ((int64_t)(dim / kw) * block_size + tok) * kw + dim % kw;",
+        "return run + (int64_t)tok * head_dim + dim;"),
+    "key slab transposed inside": (
+        "return run + ((int64_t)(dim / kw) * block_size + tok) * kw + dim % kw;",
+        "return run + ((int64_t)(dim / kw) * kw + dim % kw) * block_size + tok;"),
+    "key slab width 16": ("const int32_t kw = head_dim % 32 == 0 ? 32 : head_dim;",
+                          "const int32_t kw = head_dim % 16 == 0 ? 16 : head_dim;"),
 }
 
 

@@ -23,6 +23,38 @@ import torch.nn.functional as F
 import oracle
 
 
+def _k_slab(d):
+    return 32 if d % 32 == 0 else d
+
+
+def k_elem(d, bs, dim, tok):
+    """Element of (dim, tok) inside one (block, head) K run: slabs of 32 dims,
+    [dim / 32][tok][dim % 32] (one slab spans every dim when 32 does not
+    divide d)."""
+    kw = _k_slab(d)
+    return ((dim // kw) * bs + tok) * kw + dim % kw
+
+
+def k_pool(logical):
+    """A K pool [nb, Hkv, d * bs] from its logical form [nb, Hkv, bs, d]."""
+    nb, H, bs, d = logical.shape
+    out = torch.empty(nb, H, d * bs, dtype=logical.dtype)
+    for dim in range(d):
+        for tok in range(bs):
+            out[:, :, k_elem(d, bs, dim, tok)] = logical[:, :, tok, dim]
+    return out
+
+
+def k_logical(pool, d, bs):
+    """The logical [nb, Hkv, bs, d] view of a K pool (a copy)."""
+    flat = pool.reshape(pool.shape[0], pool.shape[1], d * bs)
+    out = torch.empty(pool.shape[0], pool.shape[1], bs, d, dtype=pool.dtype)
+    for dim in range(d):
+        for tok in range(bs):
+            out[:, :, tok, dim] = flat[:, :, k_elem(d, bs, dim, tok)]
+    return out
+
+
 def _v_tiles(d, bs):
     return (16 if d % 16 == 0 else d), (4 if bs % 4 == 0 else bs)
 
@@ -236,7 +268,7 @@ def test_prepare_empty_batch():
 @pytest.mark.parametrize("nb,H,bs,d,T", [(7, 3, 4, 8, 9), (5, 2, 8, 32, 11)])
 def test_kv_write_post_state(dtype, nb, H, bs, d, T):
     g = torch.Generator().manual_seed(3)
-    kc = torch.randn(nb, H, bs, d, generator=g).to(dtype)
+    kc = k_pool(torch.randn(nb, H, bs, d, generator=g).to(dtype))
     vc = v_pool(torch.randn(nb, H, d, bs, generator=g).to(dtype))
     key = torch.randn(T, H, d, generator=g).to(dtype)
     val = torch.randn(T, H, d, generator=g).to(dtype)
@@ -244,6 +276,7 @@ def test_kv_write_post_state(dtype, nb, H, bs, d, T):
     slots[4] = -1  # padding row: no write
     kc0, vc0 = kc.clone(), vc.clone()
     oracle.kv_write(key, val, kc, vc, slots, block_size=bs)
+    kc, kc0 = k_logical(kc, d, bs), k_logical(kc0, d, bs)
     vc, vc0 = v_logical(vc, d, bs), v_logical(vc0, d, bs)
     written = np.zeros((nb, bs), bool)
     for i, s in enumerate(slots):
@@ -258,6 +291,43 @@ def test_kv_write_post_state(dtype, nb, H, bs, d, T):
                        kc0[keep[:, None, :, None].expand_as(kc0)])
     assert torch.equal(vc[keep[:, None, None, :].expand_as(vc)],
                        vc0[keep[:, None, None, :].expand_as(vc0)])
+
+
+def test_key_layout_positions():
+    """Where one token's K row lands in the pool, element by element, for a
+    slab run (head_dim 64, block_size 8) and a plain one (head_dim 8,
+    block_size 6): the documented order written out, not k_elem."""
+    for d, bs, slot, expect in (
+            (64, 8, 2 * 8 + 5, lambda dim: (dim // 32) * 256 + 5 * 32 + dim % 32),
+            (8, 6, 1 * 6 + 4, lambda dim: 4 * 8 + dim)):
+        H = 2
+        kc = torch.zeros(4, H, d * bs)
+        vc = torch.zeros(4, H, d * bs)
+        val = (torch.arange(H * d, dtype=torch.float32) + 1).reshape(1, H, d)
+        oracle.kv_write(val, val, kc, vc, [slot], block_size=bs)
+        blk = slot // bs
+        for h in range(H):
+            for dim in range(d):
+                assert kc[blk, h, expect(dim)] == h * d + dim + 1, (d, bs, h, dim)
+        assert int((kc != 0).sum()) == H * d
+
+
+def test_key_layout_slabs_are_whole_lines():
+    """In a 16-bit K run of head_dim 128 and a 16-token block, the 16 tokens x
+    32 dims of one slab fill 8 aligned 128-byte lines and nothing else (one
+    wave-wide 16-byte load), and one token's row lands in 4 runs of 64
+    contiguous bytes."""
+    d, bs = 128, 16
+    for s in range(d // 32):
+        byte_set = {k_elem(d, bs, dim, tok) * 2 // 128 for tok in range(bs)
+                    for dim in range(32 * s, 32 * s + 32)}
+        assert byte_set == set(range(8 * s, 8 * s + 8))
+    for tok in range(bs):
+        starts = sorted(k_elem(d, bs, dim, tok) for dim in range(0, d, 32))
+        for dim0 in range(0, d, 32):
+            run = [k_elem(d, bs, dim, tok) for dim in range(dim0, dim0 + 32)]
+            assert run == list(range(run[0], run[0] + 32))
+        assert len(starts) == 4
 
 
 def test_value_layout_positions():
@@ -333,6 +403,7 @@ def make_paged(nst, nct, Hq, Hkv, d, bs, seed, dtype=torch.float32, slack=3):
             b, o = int(bt[r, j // bs]), j % bs
             kc[b, :, o, :] = Ks[r][j]
             vc[b, :, :, o] = Vs[r][j]
+    kc = k_pool(kc)
     vc = v_pool(vc)
     q = torch.cat([Qs[r][int(nct[r]):] for r in range(R)]).contiguous()
     qsl = np.concatenate([[0], np.cumsum(nst)]).astype(np.int32)
@@ -505,14 +576,14 @@ def test_prepare_write_attention_chain_equals_unpaged_sdpa():
     logical, paged = make_paged(nst, nct, 4, 2, 16, 4, seed=16)
     R = len(nst)
     # wipe this step's slots, then let prepare + kv_write put them back
-    kc, vc = paged["kc"].clone(), v_logical(paged["vc"], 16, 4)
+    kc, vc = k_logical(paged["kc"], 16, 4), v_logical(paged["vc"], 16, 4)
     key = torch.cat([logical["Ks"][r][nct[r]:] for r in range(R)]).contiguous()
     val = torch.cat([logical["Vs"][r][nct[r]:] for r in range(R)]).contiguous()
     prep = oracle.prepare(nst, nct, paged["bt"], block_size=4, num_blocks=kc.shape[0])
     for s in prep["slot_mapping"]:
         kc[s // 4, :, s % 4, :] = float("nan")
         vc[s // 4, :, :, s % 4] = float("nan")
-    vc = v_pool(vc)
+    kc, vc = k_pool(kc), v_pool(vc)
     oracle.kv_write(key, val, kc, vc, prep["slot_mapping"], block_size=4)
     out = oracle.attention(paged["q"], kc, vc, prep["query_start_loc"], prep["seq_lens"],
                            paged["bt"], 4, 0.25)
@@ -691,8 +762,8 @@ def _fp8_distinct_codes(d):
 def test_fp8_pool_byte_positions():
     """Where one token's K and V rows land in the FP8 pools, byte by byte, for
     every token position of a block and both heads of a two-head pool, written
-    out from the documented orders: K token-major
-    [block][head][token][dim]; each V (block, head) run ordered
+    out from the documented orders: each K (block, head) run ordered
+    [dim / 64][token][dim % 64]; each V (block, head) run ordered
     [dim / 64][token / 4][dim % 16][(dim / 16) % 4][token % 4].  Each element
     of the row is the exact value of a distinct code (scale 1), so its byte is
     found wherever it lands."""
@@ -711,7 +782,7 @@ def test_fp8_pool_byte_positions():
         for h in range(H):
             run = (blk * H + h) * d * bs
             for dim in range(d):
-                k_at = ((blk * H + h) * bs + tok) * d + dim
+                k_at = run + (dim // 64) * 1024 + tok * 64 + dim % 64
                 v_at = run + (dim // 64) * 1024 + (tok // 4) * 256 + (dim % 16) * 16 + \
                     ((dim // 16) % 4) * 4 + tok % 4
                 assert kflat[k_at] == codes[h][dim], ("K", tok, h, dim)

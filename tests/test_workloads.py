@@ -15,8 +15,11 @@ def test_config1_structure_and_poison():
     used = wl.block_table[wl.block_table >= 0]
     assert len(used) == 3 and len(set(used.tolist())) == 3
     # history slots are finite, everything else in the pool is NaN
-    hist = int(np.isfinite(wl.key_cache[:, 0, :, 0].numpy()).sum())
+    assert wl.key_cache.shape == (16, 2, 64 * 16)
+    k = workloads.key_logical(wl.key_cache, 64, 16)
+    hist = int(np.isfinite(k[:, 0, :, 0].numpy()).sum())
     assert hist == 14 + 0 + 9
+    assert torch.isnan(wl.key_cache).sum() == (16 * 16 - 23) * 2 * 64
     assert torch.isnan(wl.value_cache).sum() == (16 * 16 - 23) * 2 * 64
     assert wl.q.shape == (10, 4, 64) and torch.isfinite(wl.q).all()
 
@@ -86,3 +89,28 @@ def test_value_pool_order_and_inverse():
                      if tiled else dim * bs + tok)
                 assert torch.equal(pool[:, :, e], logical[:, :, dim, tok]), (d, bs, dim, tok)
         assert torch.equal(workloads.value_logical(pool, d, bs), logical)
+
+
+def test_key_pool_order_and_inverse():
+    """key_pool puts element (tok, dim) of a (block, head) run at
+    ((dim / 32) * bs + tok) * 32 + dim % 32 (plain [tok][dim] when 32 does not
+    divide d); key_logical undoes it."""
+    for d, bs in ((64, 16), (128, 4), (8, 5)):
+        logical = torch.arange(3 * 2 * bs * d, dtype=torch.float32).reshape(3, 2, bs, d)
+        pool = workloads.key_pool(logical)
+        assert pool.shape == (3, 2, d * bs)
+        kw = 32 if d % 32 == 0 else d
+        for tok in range(bs):
+            for dim in range(d):
+                at = ((dim // kw) * bs + tok) * kw + dim % kw
+                assert torch.equal(pool[:, :, at], logical[:, :, tok, dim])
+        assert torch.equal(workloads.key_logical(pool, d, bs), logical)
+
+
+def test_fp8_key_pool_order():
+    logical = torch.arange(2 * 16 * 128, dtype=torch.int32).reshape(1, 2, 16, 128)
+    pool = workloads.fp8_key_pool(logical)
+    for tok in range(16):
+        for dim in range(128):
+            assert torch.equal(pool[:, :, (dim // 64) * 1024 + tok * 64 + dim % 64],
+                               logical[:, :, tok, dim])
