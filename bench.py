@@ -366,6 +366,117 @@ class ClockReader:
                              "max": float(np.max(mclk))}}
 
 
+class Calib:
+    """The benchmark's measurement kernels (libpkv_calib.so, include/pkv_calib.h):
+    the shader clock seen by a spinning wave, and a plain read kernel over a
+    list of K/V runs.  Neither is part of the measured path."""
+
+    def __init__(self):
+        import ctypes
+        from paged_kv_cache_prepare_amd import _build
+        if not os.path.exists(_build.CALIB_LIB_PATH):
+            raise RuntimeError(f"{_build.CALIB_LIB_PATH} is not built: run __graft_entry__.build()")
+        self.lib = ctypes.CDLL(_build.CALIB_LIB_PATH)
+        P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        self.lib.pkv_calib_clock.argtypes = [P, i64, P]
+        self.lib.pkv_calib_read_runs.argtypes = [P, P, i64, i32, P, P]
+
+    def clock(self, ms, stream):
+        """Enqueue a wave that spins for ``ms`` on ``stream``; returns a
+        function giving the shader clock in MHz once the stream is done."""
+        import torch
+        with torch.cuda.stream(stream):  # allocated for this stream; the kernel writes both words
+            out = torch.empty(2, dtype=torch.int64, device=stream.device)
+        ticks = int(min(max(ms, 0.01), 9000.0) * 1e5)
+        rc = self.lib.pkv_calib_clock(out.data_ptr(), ticks, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"pkv_calib_clock: {rc}")
+        return lambda: 100.0 * float(out[0]) / float(out[1])
+
+    def read_runs(self, addrs, wave_begin, run_kib, sink, stream):
+        rc = self.lib.pkv_calib_read_runs(addrs.data_ptr(), wave_begin.data_ptr(),
+                                          wave_begin.numel() - 1, run_kib, sink.data_ptr(),
+                                          stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"pkv_calib_read_runs: {rc}")
+
+
+def decode_run_stream(wl, b):
+    """The K/V runs the decode items of ``wl``'s work list read, per wave, in
+    the order the kernels issue them: item by item as the plan lists them,
+    the item's four waves splitting its partition's 32-token steps, each
+    step's two K runs then its two V runs.  Returns (run addresses, wave
+    offsets, run KiB) as CPU int64 arrays, or None without decode items."""
+    import torch
+    ws = b["ws"].cpu()
+    head = ws[:256].view(torch.int32).numpy()
+    n = int(head[0])
+    items = ws[256:256 + 16 * n].view(torch.int32).numpy().reshape(n, 4)
+    items = items[items[:, 3] >= 1]
+    if len(items) == 0:
+        return None
+    seq = b["prep"]["seq_lens"].cpu().numpy().astype(np.int64)
+    run = 16 * wl.head_dim * wl.key_cache.element_size()
+    stride = wl.num_kv_heads * run
+    kbase, vbase = wl.key_cache.data_ptr(), wl.value_cache.data_ptr()
+    addrs, begin = [], [0]
+    for r, h, k, ns in items.tolist():
+        nblk = -(-int(seq[r]) // 16)
+        steps_all = -(-nblk // 2)
+        per_split = -(-steps_all // ns)
+        sp_b = k * per_split
+        sp_e = min(steps_all, sp_b + per_split)
+        per_wave = -(-max(0, sp_e - sp_b) // 4)
+        row = wl.block_table[r].astype(np.int64)
+        for w in range(4):
+            s = np.arange(sp_b + w * per_wave, min(sp_e, sp_b + (w + 1) * per_wave))
+            j = np.stack([2 * s, 2 * s + 1], 1)
+            ok = j < nblk
+            off = row[np.minimum(j, nblk - 1)] * stride + h * run
+            a = np.concatenate([kbase + off, vbase + off], 1)       # K0 K1 V0 V1 per step
+            a = a[np.concatenate([ok, ok], 1)]
+            addrs.append(a)
+            begin.append(begin[-1] + len(a))
+    return (np.concatenate(addrs).astype(np.int64), np.asarray(begin, np.int64), run // 1024)
+
+
+def read_ceiling(calib, wl, b, kernel_ms, unique_bytes, flush, steps, stream):
+    """Time a plain read kernel over the decode run stream of ``wl`` (each
+    iteration after the cache flush, HIP events) and compare."""
+    import torch
+    st = decode_run_stream(wl, b)
+    if st is None:
+        return None
+    addrs, begin, kib = st
+    dev = wl.q.device
+    a_d = torch.from_numpy(addrs).to(dev)
+    b_d = torch.from_numpy(begin).to(dev)
+    sink = torch.empty(64 * (len(begin) - 1), dtype=torch.int32, device=dev)
+    for _ in range(2):
+        flush()
+        calib.read_runs(a_d, b_d, kib, sink, stream)
+    ts = []
+    for _ in range(steps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        calib.read_runs(a_d, b_d, kib, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ts.append(e0.elapsed_time(e1))
+    ms = pct(ts)
+    t = ms["median"] / 1e3
+    logical = int(len(addrs)) * kib * 1024
+    return {"reader_ms": ms, "runs": int(len(addrs)), "logical_bytes": logical,
+            "reader_logical_gbs": round(logical / t / 1e9, 1),
+            "reader_frac_of_peak": round(unique_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_over_reader_time": round(kernel_ms / ms["median"], 4),
+            "note": "a plain read kernel (no arithmetic, the same non-temporal loads, 8 runs in "
+                    "flight per wave) over exactly the K/V runs the decode items read, in the "
+                    "work list's order; reader_frac_of_peak is the roofline fraction that "
+                    "reader attains on the same algorithmic bytes"}
+
+
 def pct(xs):
     xs = np.asarray(xs, np.float64)
     return {"median": round(float(np.median(xs)), 4), "p10": round(float(np.percentile(xs, 10)), 4),
@@ -664,6 +775,11 @@ def main():
         flush()
         step()
     clock_reader = ClockReader()
+    try:
+        calib = Calib()
+    except Exception as exc:  # measurement extras only: the bench line stands without them
+        print(f"calibration kernels unavailable: {exc}", file=sys.stderr)
+        calib = None
     # timed region: K steps, each after a flush, each bracketed by events
     ev = [events(2) for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
@@ -720,21 +836,52 @@ def main():
                                              + ("_fp8" if args.kv_dtype == "fp8" else ""))
             sub_lines[name] = {"rows": sw.num_tokens, "requests": sw.num_reqs,
                                "run_ms": ms, **sr}
+            if name == "decode" and calib is not None:
+                sub_lines[name]["read_ceiling"] = read_ceiling(
+                    calib, sw, sb, ms["median"], algorithmic_work(sw)["bytes_unique"], flush,
+                    args.steps, stream)
             del sb
+    run_ceiling = None
+    if calib is not None and len(subs["prefill"]) == 0 and args.rows != "prefill":
+        run_ceiling = read_ceiling(calib, wl, b, pct(phase_ms["run"])["median"],
+                                   work["bytes_unique"], flush, args.steps, stream)
 
     # clocks while the attention run executes: --clock-runs runs queued back
-    # to back (no flush), read until the last one ends
+    # to back (no flush).  The shader clock comes from a wave that spins on a
+    # second stream from the end of the second run for 80 % of the expected
+    # rest; the memory clock from amdsmi, read until the last run ends.
     done_ev = torch.cuda.Event()
+    start_ev = torch.cuda.Event()
+    side = torch.cuda.Stream(dev)
+    wave_clock = {}
 
     def enqueue():
-        for _ in range(args.clock_runs):
+        for i in range(args.clock_runs):
             run()
+            if i == 1:
+                start_ev.record(stream)
         done_ev.record(stream)
+        if calib is not None and args.clock_runs > 2:
+            side.wait_event(start_ev)
+            spin = 0.8 * pct(phase_ms["run"])["median"] * (args.clock_runs - 2)
+            wave_clock["under_load"] = calib.clock(spin, side)
 
     if args.clock_runs > 0:
-        clocks = clock_reader.under_load(enqueue, done_ev.query)
-        clocks["note"] = (f"sampled while {args.clock_runs} attention runs of the workload "
-                          "executed back to back")
+        amd = clock_reader.under_load(enqueue, done_ev.query)
+        torch.cuda.synchronize(dev)
+        clocks = {"sclk_mhz": None, "mclk_mhz": None}
+        if "under_load" in wave_clock:
+            clocks["sclk_mhz"] = round(wave_clock["under_load"](), 1)
+            idle = calib.clock(20.0, side)
+            torch.cuda.synchronize(dev)
+            clocks["sclk_idle_mhz"] = round(idle(), 1)
+            clocks["sclk_source"] = ("one wave spinning on a second stream beside the runs: "
+                                     "s_memtime ticks over s_memrealtime (100 MHz) ticks; "
+                                     "sclk_idle_mhz is the same wave alone")
+        if isinstance(amd.get("mclk_mhz"), dict):
+            clocks["mclk_mhz"] = amd["mclk_mhz"]["median"]
+            clocks["mclk_source"] = f"{amd['source']}, {amd['samples']} samples"
+        clocks["note"] = (f"{args.clock_runs} attention runs of the workload back to back")
     else:
         clocks = {"note": "not read (--clock-runs 0)"}
     torch.cuda.synchronize(dev)
@@ -773,6 +920,8 @@ def main():
     roof["rule"] = "frac = max(t_bytes, t_flops) / t"
     if sub_lines:
         roof["sub_batches"] = sub_lines
+    if run_ceiling is not None:
+        roof["read_ceiling"] = run_ceiling
 
     cpu = cpu_baseline(wl, args.cpu_seconds, args.cpu_single_seconds)
     line = {

@@ -1,9 +1,12 @@
-"""Build libpkv.so and libpkv_checked.so (HIP, gfx950) in-tree with hipcc.
+"""Build libpkv.so, libpkv_checked.so and libpkv_calib.so (HIP, gfx950)
+in-tree with hipcc.
 
 Every source under csrc/ is compiled to an object in parallel and linked
 into ``paged_kv_cache_prepare_amd/libpkv.so``.  The checked build
 (``libpkv_checked.so``) links the same kernels with api.hip compiled again
-under ``PKV_DEBUG_CHECKS`` and the validation kernels of checks.hip.
+under ``PKV_DEBUG_CHECKS`` and the validation kernels of checks.hip.  The
+benchmark's measurement kernels (csrc/calib/calib.hip, include/pkv_calib.h)
+are a library of their own, ``libpkv_calib.so``.
 Packed-fp32 instructions are switched off for all device code
 (``-packed-fp32-ops``).  ``FILE_FLAGS`` adds per-file options.
 """
@@ -21,6 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 CHECKED_LIB_PATH = os.path.join(HERE, "libpkv_checked.so")
+CALIB_LIB_PATH = os.path.join(HERE, "libpkv_calib.so")
 KERNEL_SOURCES = ["prepare.hip", "kv_write.hip", "block_ops.hip", "attention.hip"]
 SOURCES = ["api.hip", *KERNEL_SOURCES]
 # Per-file flags.  The attention kernels never feed a NaN into a max or a sum
@@ -62,14 +66,20 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         return obj
 
     jobs = [(src, src.rsplit(".", 1)[0] + ".o", []) for src in SOURCES]
-    jobs += [("api.hip", "api_checked.o", ["-DPKV_DEBUG_CHECKS"]), ("checks.hip", "checks.o", [])]
+    jobs += [("api.hip", "api_checked.o", ["-DPKV_DEBUG_CHECKS"]), ("checks.hip", "checks.o", []),
+             (os.path.join("calib", "calib.hip"), "calib.o", [])]
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
         objs = dict(zip((j[1] for j in jobs), ex.map(one, jobs)))
     kernels = [objs[src.rsplit(".", 1)[0] + ".o"] for src in KERNEL_SOURCES]
     for path, own in ((LIB_PATH, [objs["api.o"]]),
-                      (CHECKED_LIB_PATH, [objs["api_checked.o"], objs["checks.o"]])):
+                      (CHECKED_LIB_PATH, [objs["api_checked.o"], objs["checks.o"]]),
+                      (CALIB_LIB_PATH, [objs["calib.o"]])):
+        if path == CALIB_LIB_PATH:
+            kernels_of = []
+        else:
+            kernels_of = kernels
         tmp = path + ".tmp"
-        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *own, *kernels, "-o", tmp]
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *own, *kernels_of, "-o", tmp]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
