@@ -471,7 +471,7 @@ def read_ceiling(calib, wl, b, kernel_ms, unique_bytes, flush, steps, stream):
             "reader_logical_gbs": round(logical / t / 1e9, 1),
             "reader_frac_of_peak": round(unique_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_over_reader_time": round(kernel_ms / ms["median"], 4),
-            "note": "a plain read kernel (no arithmetic, the same non-temporal loads, 8 runs in "
+            "note": "a plain read kernel (no arithmetic, the same non-temporal loads, 32 KiB in "
                     "flight per wave) over exactly the K/V runs the decode items read, in the "
                     "work list's order; reader_frac_of_peak is the roofline fraction that "
                     "reader attains on the same algorithmic bytes"}

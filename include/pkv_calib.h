@@ -38,7 +38,8 @@ int pkv_calib_clock(uint64_t* out, int64_t ticks_100mhz, void* stream);
 /*
  * Wave w of the launch reads the runs of run_kib KiB at device addresses
  * run_addr[wave_begin[w]] .. run_addr[wave_begin[w + 1] - 1] in order,
- * eight runs in flight, with non-temporal 16-byte loads (the cache policy
+ * 32 KiB in flight (8 runs of 4 KiB, 16 of 2 KiB, 32 of 1 KiB), with
+ * non-temporal 16-byte loads (the cache policy
  * the decode kernels use for their K/V stream), and writes the XOR of every
  * 32-bit word it read, per lane, to sink[64 w + lane].
  *   run_addr       uint64 [wave_begin[num_waves]]: each a device address of
@@ -46,8 +47,8 @@ int pkv_calib_clock(uint64_t* out, int64_t ticks_100mhz, void* stream);
  *                  (precondition)
  *   wave_begin     int64 [num_waves + 1], non-decreasing, wave_begin[0] = 0
  *   num_waves      host, >= 1
- *   run_kib        host, 1 .. 4 (a 16-bit K or V run of a 16-token block is
- *                  4 KiB at head_dim 128, an FP8 one 2 KiB)
+ *   run_kib        host, 1, 2 or 4 (a 16-bit K or V run of a 16-token block
+ *                  is 4 KiB at head_dim 128, an FP8 one 2 KiB)
  *   sink           uint32 [64 * num_waves]
  */
 int pkv_calib_read_runs(const uint64_t* run_addr, const int64_t* wave_begin, int64_t num_waves,

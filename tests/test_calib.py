@@ -39,3 +39,4 @@ def test_rejects_bad_arguments():
     assert lib.pkv_calib_read_runs(p, p, 0, 4, p, None) == 1
     assert lib.pkv_calib_read_runs(p, p, 1, 0, p, None) == 1
     assert lib.pkv_calib_read_runs(p, p, 1, 5, p, None) == 1
+    assert lib.pkv_calib_read_runs(p, p, 1, 3, p, None) == 1
