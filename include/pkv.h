@@ -371,7 +371,10 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
  *                   finite and > 0
  *   dtype           PKV_BF16 (MFMA path) or PKV_F32 (fp32 vector path)
  *   split_tokens    host, partition size (tokens) for splitting one long
- *                   decode context over several workgroups; 0 = automatic;
+ *                   decode context over several workgroups; 0 = automatic
+ *                   (partitions only when requests x kv heads is below the
+ *                   current device's CU count, into about one item per CU:
+ *                   size the workspace with the same device current);
  *                   otherwise a positive multiple of 32
  *   workspace, workspace_bytes  device scratch of at least
  *                   pkv_paged_attention_workspace_bytes(...) bytes, 256-byte

@@ -1771,11 +1771,14 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
   const int64_t pairs_per_req = (int64_t)num_reqs * num_kv_heads;
   int32_t st = split_tokens;
   if (st == 0) {
-    // Partition long decode contexts only when the batch alone cannot fill
-    // the chip: aim for ~2048 workgroups of at least 256 tokens each.  A
-    // batch of one request with more query rows than one decode tile holds
-    // no decode item, so it gets no partitions (and no reduce launch).
-    const int64_t want = 2048;
+    // Partition long decode contexts only when the batch has fewer
+    // (request, kv head) items than the chip has CUs, and then into about
+    // one item per CU, each of at least 256 tokens: more, shorter items
+    // measured slower (each pays its own set-up and merge, and a shared
+    // prefix's partitions run less in step).  A batch of one request with
+    // more query rows than one decode tile holds no decode item, so it gets
+    // no partitions (and no reduce launch).
+    const int64_t want = device_cu_count();
     const bool one_prompt = num_reqs == 1 && (int64_t)max_query_len * p.group > kPairsPerTile;
     if (pairs_per_req >= want || max_seq_len <= 256 || one_prompt) {
       st = ((std::max(max_seq_len, 1) + 31) / 32) * 32;

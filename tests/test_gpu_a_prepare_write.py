@@ -138,7 +138,7 @@ def _kv_case(T, H, d, bs, nb, dtype, seed, consecutive):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 96, 40])   # 96: three K slabs; 40: plain K and V runs
 @pytest.mark.parametrize("bs", [16, 4, 5])
 @pytest.mark.parametrize("consecutive", [False, True])
 def test_kv_write_vs_oracle(dtype, d, bs, consecutive):
