@@ -318,7 +318,9 @@ pkv_status pkv_kv_cache_write_fp8(const void* key, const void* value, int64_t ke
  * pkv_paged_attention_varlen needs for these host-side sizes (the work list
  * and, for long decode contexts split into partitions, the per-partition
  * partial results).  The arguments mean what they mean there; split_tokens = 0
- * selects the library's own partition size.  Returns 0 for invalid sizes.
+ * selects the library's own partition size, which depends on the current
+ * device's CU count (call this with the device of the attention call
+ * current).  Returns 0 for invalid sizes.
  */
 size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
                                            int32_t num_q_heads, int32_t num_kv_heads,
@@ -442,7 +444,8 @@ pkv_status pkv_paged_attention_varlen_fp8(
  * pkv_paged_attention_varlen* call) made with the same query_start_loc and
  * seq_lens contents and the same num_reqs, num_tokens, max_query_len,
  * max_seq_len, num_q_heads, num_kv_heads, head_dim, dtype and split_tokens,
- * enqueued earlier on the same stream (or ordered before it), with no other
+ * on the same device, enqueued earlier on the same stream (or ordered before
+ * it), with no other
  * call using the workspace in between.  Runs over one workspace must not
  * overlap: they share its partition buffers.  The checked build verifies the
  * list's record of the sizes and a checksum of the batch (PKV_CHECK_PLAN);
