@@ -132,6 +132,29 @@ def test_attention_forced_partitions(split_tokens):
     assert_attention_close(many, ref, wl.dtype, f"split {split_tokens}")
 
 
+def test_attention_automatic_partitions_of_uneven_contexts():
+    """The library's own partition size on a batch with fewer (request, kv
+    head) items than CUs: contexts of very different lengths get different
+    partition counts (here 1, 2 and 11 at the 3776-token size a 256-CU GPU
+    picks), and the rows match the oracle; so does the same batch with FP8
+    pools."""
+    nst = [1, 1, 1]
+    nct = [99, 4999, 39999]
+    wl = workloads.build("autosplit", nst, nct, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         seed=78, device=device(), pool_slack=1.1)
+    need0 = pkv.attention_workspace_bytes(3, 3, 32, 8, 128, 1, 40000, 0, wl.dtype)
+    need1 = pkv.attention_workspace_bytes(3, 3, 32, 8, 128, 1, 40000, 40000 // 32 * 32 + 32,
+                                          wl.dtype)
+    assert need0 > need1, "the automatic choice partitions this batch"
+    _, _, _, out = gpu_step(wl)
+    _, _, _, ref = oracle_step(wl)
+    assert_attention_close(out, ref, wl.dtype, "automatic partitions")
+    f8 = workloads.to_fp8(wl, 0.0125, 0.0125)
+    _, _, _, out8 = gpu_step(f8)
+    _, _, _, ref8 = oracle_step(f8)
+    assert_attention_close(out8, ref8, wl.dtype, "automatic partitions, FP8 pools")
+
+
 def test_attention_many_requests():
     """More requests than the work-list builder ranks at once (1024): the list
     is built chunk by chunk in request order and must still cover every row."""
