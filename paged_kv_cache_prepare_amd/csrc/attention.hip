@@ -471,7 +471,15 @@ constexpr int kRsrcWord3 = 0x00020000;
 // items at most), and the streaming policy sustains a markedly higher read
 // rate on scattered 4 KB runs.  Prefill tiles keep the default policy: every
 // tile of a prompt chunk re-reads the same blocks, which must stay cached.
+// One exception: in a launch that also holds prompt tiles, a partition of a
+// split context whose first block another request holds at the same position
+// (a shared prefix) is read with the default policy.  Beside the prompt
+// tiles' cached lines the streaming lines of a shared run are evicted before
+// the slower sharers reach them; with the default policy they stay long
+// enough to be read once from memory.  In a decode-only launch the sharers
+// keep step and the streaming policy stays faster.
 constexpr int kKvLoadPolicy = 2;
+constexpr int kSharedKvLoadPolicy = 0;
 constexpr int kPrefillLoadPolicy = 0;
 
 // Descriptor of one (block, kv head) run of a pool.  Its record count bounds
@@ -488,18 +496,18 @@ struct StepRsrc {
   bool ok0, ok1;
 };
 
-template <int D>
+template <int D, int POL>
 __device__ inline void issue_step_loads(StepLoads<D>& ld, const StepRsrc& r, int k_lane,
                                         int v_lane) {
 #pragma unroll
   for (int s = 0; s < Geometry<D>::KS; ++s) {
-    ld.k0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + s * 1024, 0, kKvLoadPolicy));
-    ld.k1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + s * 1024, 0, kKvLoadPolicy));
+    ld.k0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + s * 1024, 0, POL));
+    ld.k1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + s * 1024, 0, POL));
   }
 #pragma unroll
   for (int dt = 0; dt < Geometry<D>::DT; ++dt) {
-    ld.v0[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v0, v_lane + dt * (16 * kBlock * 2), 0, kKvLoadPolicy);
-    ld.v1[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v1, v_lane + dt * (16 * kBlock * 2), 0, kKvLoadPolicy);
+    ld.v0[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v0, v_lane + dt * (16 * kBlock * 2), 0, POL);
+    ld.v1[dt] = __builtin_amdgcn_raw_buffer_load_b64(r.v1, v_lane + dt * (16 * kBlock * 2), 0, POL);
   }
 }
 
@@ -615,7 +623,7 @@ __device__ inline StepRsrc make_step(const AttnArgs& a, int b0, int b1, const ch
 // never force the in-flight K/V loads to drain).  Steps whose keys all lie at
 // or below p_unmasked (and whose blocks are valid) skip the causal / tail
 // masking.
-template <int D, int NT>
+template <int D, int NT, int POL>
 __device__ __attribute__((always_inline)) inline void walk_steps(
     TileState<D> (&st)[NT], const bf16x8 (&qf)[NT][Geometry<D>::KS], const int (&p_col)[NT],
     const AttnArgs& a, table_t* bt, int nblk, int s_begin, int s_end,
@@ -658,19 +666,19 @@ __device__ __attribute__((always_inline)) inline void walk_steps(
   StepLoads<D> A, B;
   int2 ids = ids_at(s_begin);
   StepRsrc sa = make_step<D>(a, ids.x, ids.y, kbase, vbase), sbk;
-  issue_step_loads<D>(A, sa, k_lane, v_lane);
+  issue_step_loads<D, POL>(A, sa, k_lane, v_lane);
   ids = ids_at(s_begin + 1);
   int step = s_begin;
   while (true) {
     // past the end the ids are -1: zero-count descriptors, no memory traffic
     sbk = make_step<D>(a, ids.x, ids.y, kbase, vbase);
     ids = ids_at(step + 2);
-    issue_step_loads<D>(B, sbk, k_lane, v_lane);
+    issue_step_loads<D, POL>(B, sbk, k_lane, v_lane);
     compute(A, sa, step);
     if (++step >= s_end) break;
     sa = make_step<D>(a, ids.x, ids.y, kbase, vbase);
     ids = ids_at(step + 2);
-    issue_step_loads<D>(A, sa, k_lane, v_lane);
+    issue_step_loads<D, POL>(A, sa, k_lane, v_lane);
     compute(B, sbk, step);
     if (++step >= s_end) break;
   }
@@ -737,18 +745,18 @@ __device__ inline StepRsrc make_step8(const AttnArgs& a, int b0, int b1, const c
   return r;
 }
 
-template <int D>
+template <int D, int POL>
 __device__ inline void issue_step_loads8(StepLoads8<D>& ld, const StepRsrc& r, int k_lane,
                                          int v_lane) {
 #pragma unroll
   for (int t = 0; t < Geometry8<D>::KL; ++t) {
-    ld.k0[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + 1024 * t, 0, kKvLoadPolicy);
-    ld.k1[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + 1024 * t, 0, kKvLoadPolicy);
+    ld.k0[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k0, k_lane + 1024 * t, 0, POL);
+    ld.k1[t] = __builtin_amdgcn_raw_buffer_load_b128(r.k1, k_lane + 1024 * t, 0, POL);
   }
 #pragma unroll
   for (int q = 0; q < Geometry8<D>::VL; ++q) {
-    ld.v0[q] = __builtin_amdgcn_raw_buffer_load_b128(r.v0, v_lane + 1024 * q, 0, kKvLoadPolicy);
-    ld.v1[q] = __builtin_amdgcn_raw_buffer_load_b128(r.v1, v_lane + 1024 * q, 0, kKvLoadPolicy);
+    ld.v0[q] = __builtin_amdgcn_raw_buffer_load_b128(r.v0, v_lane + 1024 * q, 0, POL);
+    ld.v1[q] = __builtin_amdgcn_raw_buffer_load_b128(r.v1, v_lane + 1024 * q, 0, POL);
   }
 }
 
@@ -815,7 +823,7 @@ __device__ inline void tile_step8(TileState<D>& st, const bf16x8* qf, const Step
 
 // walk_steps over FP8 pools (same pipeline: loads of step s+1 in flight while
 // step s is computed).
-template <int D>
+template <int D, int POL>
 __device__ __attribute__((always_inline)) inline void walk_steps8(
     TileState<D>& st, const bf16x8 (&qf)[Geometry<D>::KS], int p_col, const AttnArgs& a,
     table_t* bt, int nblk, int s_begin, int s_end, int p_unmasked, int seq_len,
@@ -845,18 +853,18 @@ __device__ __attribute__((always_inline)) inline void walk_steps8(
   StepLoads8<D> A, B;
   int2 ids = ids_at(s_begin);
   StepRsrc sa = make_step8<D>(a, ids.x, ids.y, kbase, vbase), sbk;
-  issue_step_loads8<D>(A, sa, k_lane, v_lane);
+  issue_step_loads8<D, POL>(A, sa, k_lane, v_lane);
   ids = ids_at(s_begin + 1);
   int step = s_begin;
   while (true) {
     sbk = make_step8<D>(a, ids.x, ids.y, kbase, vbase);
     ids = ids_at(step + 2);
-    issue_step_loads8<D>(B, sbk, k_lane, v_lane);
+    issue_step_loads8<D, POL>(B, sbk, k_lane, v_lane);
     compute(A, sa, step);
     if (++step >= s_end) break;
     sa = make_step8<D>(a, ids.x, ids.y, kbase, vbase);
     ids = ids_at(step + 2);
-    issue_step_loads8<D>(A, sa, k_lane, v_lane);
+    issue_step_loads8<D, POL>(A, sa, k_lane, v_lane);
     compute(B, sbk, step);
     if (++step >= s_end) break;
   }
@@ -878,7 +886,7 @@ struct DecodeSmem {
 template <int D, bool KV8>
 __device__ void run_decode(const AttnArgs& a, int group, float c2, float vs, int r, int kvh,
                            int split, int nsplit, int max_splits, float* __restrict__ ml,
-                           float* __restrict__ opart, DecodeSmem<D>& sm) {
+                           float* __restrict__ opart, DecodeSmem<D>& sm, bool with_prompts) {
   using Geo = Geometry<D>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -921,14 +929,42 @@ __device__ void run_decode(const AttnArgs& a, int group, float c2, float vs, int
   const char* kbase = static_cast<const char*>(a.key_cache) + kvh * run;
   const char* vbase = static_cast<const char*>(a.value_cache) + kvh * run;
 
+  // A partition whose first block another request holds at the same position
+  // (a shared prefix) is read with the default cache policy when prompt tiles
+  // share the launch (kSharedKvLoadPolicy; 16-bit pools only: a second FP8
+  // walk measured slower on every FP8 launch, shared or not).  Only split
+  // contexts are checked: they exist when the batch has few (request, kv
+  // head) items, so the check reads at most a few hundred table entries, once
+  // per item.
+  bool shared = false;
+  if (!KV8 && with_prompts && nsplit > 1) {
+    const int j0 = 2 * sp_begin;
+    const int id0 = (j0 < nblk && j0 < a.bt_stride) ? bt[j0] : -1;
+    bool hit = false;
+    if (id0 >= 0 && id0 < a.num_blocks) {
+      for (int rr = threadIdx.x; rr < a.num_reqs; rr += kThreads) {
+        if (rr == r) continue;
+        const int len = a.seq_lens[rr];
+        if (len > 0 && j0 < ceil_div(len, kBlock) && a.block_table[(int64_t)rr * a.bt_stride + j0] == id0)
+          hit = true;
+      }
+    }
+    shared = __syncthreads_or(hit);
+  }
+
   TileState<D> st[1];
   tile_init(st[0]);
-  if (KV8)
-    walk_steps8<D>(st[0], qf[0], p_col[0], a, bt, nblk, w_begin, w_end, L - q_len, L, kbase,
-                   vbase, c2);
-  else
-    walk_steps<D, 1>(st, qf, p_col, a, bt, nblk, w_begin, w_end, L - q_len, L, kbase, vbase,
-                     c2);
+  if (KV8) {
+    walk_steps8<D, kKvLoadPolicy>(st[0], qf[0], p_col[0], a, bt, nblk, w_begin, w_end,
+                                  L - q_len, L, kbase, vbase, c2);
+  } else {
+    if (shared)
+      walk_steps<D, 1, kSharedKvLoadPolicy>(st, qf, p_col, a, bt, nblk, w_begin, w_end,
+                                            L - q_len, L, kbase, vbase, c2);
+    else
+      walk_steps<D, 1, kKvLoadPolicy>(st, qf, p_col, a, bt, nblk, w_begin, w_end, L - q_len,
+                                      L, kbase, vbase, c2);
+  }
 
   // merge the four waves' states
   const float l_tot = column_sum(st[0].l);
@@ -1548,7 +1584,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int idx = n_pre + (b - P);
   if (idx >= n) return;
   const int4 it = items[idx];
-  run_decode<D, KV8>(a, group, c2k, vs, it.x, it.y, it.z, it.w, max_splits, ml, opart, sm.dec);
+  run_decode<D, KV8>(a, group, c2k, vs, it.x, it.y, it.z, it.w, max_splits, ml, opart, sm.dec,
+                     n_pre > 0);
 }
 
 // ---------------------------------------------------------------------------

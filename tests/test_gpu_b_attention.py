@@ -313,6 +313,25 @@ def test_attention_prefix_that_diverges_and_rejoins():
         assert_attention_close(out, ref, wl.dtype, f"diverging prefix, split {st}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,d", [(16, 2, 128), (16, 4, 64)])
+def test_attention_shared_prefix_beside_prompt_tiles(Hq, Hkv, d):
+    """Split decode contexts with shared prefixes in a launch that also holds
+    prompt tiles: partitions whose first block another request holds at the
+    same position take the shared-prefix load path.  Request 5 shares only
+    block 0 with request 0, so its first partition starts on a shared block
+    and then diverges."""
+    nst = [1] * 6 + [40]
+    nct = [900, 950, 1000, 700, 640, 300, 64]
+    wl = workloads.build(f"shared_mixed_{d}", nst, nct, num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=d, seed=57, device=device(), pool_slack=1.2,
+                         shared_prefix_groups=[([0, 1, 2], 512), ([3, 4], 256)])
+    wl.block_table[5, 0] = wl.block_table[0, 0]
+    _, _, _, ref = oracle_step(wl)
+    for st in (0, 64, 256):
+        _, _, _, out = gpu_step(wl, split_tokens=st)
+        assert_attention_close(out, ref, wl.dtype, f"shared prefix beside prompt, split {st}")
+
+
 def _shape_scores(wl, growth, seed):
     """Give every key of kv head h the direction u_h scaled by growth[r](pos),
     plus noise, and every query of that head's group u_h plus noise, so that a
