@@ -1081,6 +1081,21 @@ struct PrefillLayout {
   static constexpr int total = 2 * kBytes + 2 * vBytes;
 };
 
+// FP8 pools: each wave copies its block's K and V runs into a double-buffered
+// staging area and the MFMA operands are widened from there in registers.
+// V runs are copied verbatim.  K runs are stored in 16-byte units swizzled
+// within each 64-dim slab (token t's unit of dims 16 c .. + 15 at unit
+// 4 t + (c + 2 ((t / 8) % 2)) % 4), 16 bytes apart from block to block, so
+// that the 16 lanes of one operand read hit 16 different bank groups.
+template <int D>
+struct PrefillLayout8 {
+  static constexpr int kRun = kBlock * D + 16;
+  static constexpr int vRun = kBlock * D;
+  static constexpr int kOff0 = 0, kOff1 = 4 * kRun;
+  static constexpr int vOff0 = 8 * kRun, vOff1 = 8 * kRun + 4 * vRun;
+  static constexpr int total = 8 * kRun + 8 * vRun;
+};
+
 template <int D>
 struct PrefillSmem {
   char bytes[PrefillLayout<D>::total];
@@ -1227,6 +1242,50 @@ __device__ __attribute__((always_inline)) inline void prefill_v_read(
     vf[dt] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
   }
 }
+// FP8 forms of the two operand reads.  K: lane (n, g) of tile t of half h
+// reads token 8 ((n / 4) % 2) + 4t + n % 4 of block 2h + n / 8 (the row order
+// of prefill_qk_half), dims 64 s + 16 g .. + 15 of each slab s: the A operands
+// of k-steps 2s (first 8 codes) and 2s + 1 (Q is loaded in the same order).
+// `kb` carries the lane's offset within a tile-0 read.
+template <int D, int NT>
+__device__ __attribute__((always_inline)) inline void prefill_qk_half8(
+    f32x4 (&s)[NT][2], const bf16x8 (&qf)[NT][Geometry<D>::KS], const char* kb, int h,
+    const float (&mref)[NT]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bf16x8 kf[Geometry<D>::KS];
+#pragma unroll
+    for (int sl = 0; sl < D / 64; ++sl) {
+      const u32x4 w = lds_ld<u32x4>(kb, 2 * h * PrefillLayout8<D>::kRun + 256 * t + 1024 * sl);
+      kf[2 * sl] = fp8x8_to_bf16(w.x, w.y);
+      kf[2 * sl + 1] = fp8x8_to_bf16(w.z, w.w);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 acc = {-mref[nt], -mref[nt], -mref[nt], -mref[nt]};
+#pragma unroll
+      for (int k = 0; k < Geometry<D>::KS; ++k) acc = mfma_bf16(kf[k], qf[nt][k], acc);
+      s[nt][t] = acc;
+    }
+  }
+}
+
+// V: lane (n, g) reads, for each 64-dim group dq, the two 16-byte units of
+// token groups 2 (g % 2) and 2 (g % 2) + 1 of block 2h + g / 2: word j of
+// each holds 4 tokens of dim 64 dq + 16 j + n, so the pair is the V^T operand
+// (keys 8 g .. + 7 of the half) of dim tile 4 dq + j.
+template <int D>
+__device__ __attribute__((always_inline)) inline void prefill_v_read8(
+    bf16x8 (&vf)[Geometry<D>::DT], const char* vb, int h) {
+#pragma unroll
+  for (int dq = 0; dq < D / 64; ++dq) {
+    const u32x4 lo = lds_ld<u32x4>(vb, 2 * h * PrefillLayout8<D>::vRun + 1024 * dq);
+    const u32x4 hi = lds_ld<u32x4>(vb, 2 * h * PrefillLayout8<D>::vRun + 1024 * dq + 256);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vf[4 * dq + j] = fp8x8_to_bf16(lo[j], hi[j]);
+  }
+}
+
 // O^T += V^T P^T over keys 32h..32h+31, and the denominators (an all-ones A
 // operand sums exactly the bf16 weights the numerator uses).
 template <int D, int NT>
@@ -1245,27 +1304,39 @@ __device__ __attribute__((always_inline)) inline void prefill_pv_half(
 // One 64-key step of a prefill tile from the staged K (kb) and V (vb) runs.
 // `mask` (wave-uniform) is set on the diagonal steps and on steps with an
 // unreadable block; only those pay for the per-key selects.
-template <int D, int NT>
+template <int D, int NT, bool KV8>
 __device__ __attribute__((always_inline)) inline void prefill_step(
     f32x4 (&o)[NT][Geometry<D>::DT], f32x4 (&lacc)[NT], float (&mref)[NT], bool (&has_ref)[NT],
     const bf16x8 (&qf)[NT][Geometry<D>::KS], const char* kb, const char* vb, bool mask,
     unsigned valid, int step, const int (&p_col)[NT], bf16x8 ones) {
   f32x4 s0[NT][2], s1[NT][2];
   bf16x8 p0[NT], p1[NT];
+  auto qk_half = [&](f32x4 (&sx)[NT][2], int h) {
+    if constexpr (KV8)
+      prefill_qk_half8<D, NT>(sx, qf, kb, h, mref);
+    else
+      prefill_qk_half<D, NT>(sx, qf, kb, h, mref);
+  };
+  auto v_read = [&](bf16x8 (&vx)[Geometry<D>::DT], int h) {
+    if constexpr (KV8)
+      prefill_v_read8<D>(vx, vb, h);
+    else
+      prefill_v_read<D>(vx, vb, h);
+  };
   // The two MFMA-only stretches (QK of half 0, PV of half 1) run at raised
   // wave priority, so the SIMD's other wave gets the issue slots for its
   // vector work while this one keeps the matrix unit fed.
   __builtin_amdgcn_s_setprio(1);
-  prefill_qk_half<D, NT>(s0, qf, kb, 0, mref);
+  qk_half(s0, 0);
   __builtin_amdgcn_s_setprio(0);
   if (mask) prefill_mask_half<NT>(s0, valid, step, 0, p_col);
-  prefill_qk_half<D, NT>(s1, qf, kb, 1, mref);
+  qk_half(s1, 1);
   bf16x8 vf[Geometry<D>::DT];
-  prefill_v_read<D>(vf, vb, 0);
+  v_read(vf, 0);
   prefill_softmax_half<D, NT>(p0, s0, s1, o, lacc, mref, has_ref);
   if (mask) prefill_mask_half<NT>(s1, valid, step, 1, p_col);
   prefill_pv_half<D, NT>(o, lacc, p0, vf, ones);
-  prefill_v_read<D>(vf, vb, 1);
+  v_read(vf, 1);
   prefill_softmax_half<D, NT>(p1, s1, s0, o, lacc, mref, has_ref);
   __builtin_amdgcn_s_setprio(1);
   prefill_pv_half<D, NT>(o, lacc, p1, vf, ones);
@@ -1273,10 +1344,9 @@ __device__ __attribute__((always_inline)) inline void prefill_step(
 }
 
 // KV8: the pools hold FP8 E4M3 codes (c2 already carries k_scale, vs is
-// v_scale).  Each wave then copies its block's FP8 runs into a staging area
-// (the space of the second 16-bit buffer) and, once all waves have finished
-// the current step, widens them into the single 16-bit buffer in the layout
-// below: two barriers per step instead of one.
+// v_scale).  Each wave then copies its block's FP8 runs into the
+// double-buffered FP8 staging area (PrefillLayout8) and every wave widens its
+// operands from there in registers, with the same one barrier per step.
 template <int D, bool KV8>
 __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, int r, int kvh,
                             int mtile, PrefillSmem<D>& sm) {
@@ -1308,7 +1378,9 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
                        ((int64_t)(row0 + t) * a.q_stride + (int64_t)head * D) * 2;
 #pragma unroll
     for (int s = 0; s < Geo::KS; ++s) {
-      bf16x8 v = ok ? ld_b128(qrow + (32 * s + 8 * g) * 2)
+      // FP8 pools contract the dims of k-step s in the order of their K slabs
+      const int dim = KV8 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
+      bf16x8 v = ok ? ld_b128(qrow + dim * 2)
                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
       // scores come out in log2 units: Q carries scale * log2(e), rounded
       // once to bf16 (2^-9 relative per element, well below the bf16
@@ -1358,12 +1430,12 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
   // Issue this wave's copy of block `wave` of a step into LDS buffer `buf`.
   // Returns whether the block is readable (inside the context, id inside the
   // pool); a block that is not is not read at all.
-  // FP8 staging: wave w's K run at stage + 2w * kRun8, its V run after it,
-  // both copied verbatim (lane i of copy c fills bytes 1024c + 16i).
-  constexpr int kRun8 = Geometry8<D>::kHeadBytes;
-  static_assert(!KV8 || 8 * kRun8 <= Lay::kBytes, "FP8 stage must fit one 16-bit K area");
-  char* stage_k = sm.bytes + Lay::kOff1 + 2 * wave * kRun8;
-  char* stage_v = stage_k + kRun8;
+  // FP8 copies of wave w's block: V verbatim; K slab c with lane i's unit from
+  // token i / 4, dims 16 ((i % 4 - 2 ((i / 32) % 2)) % 4) .. + 15 (the swizzle
+  // of PrefillLayout8).
+  using L8 = PrefillLayout8<D>;
+  static_assert(!KV8 || L8::total <= Lay::total, "FP8 staging must fit the 16-bit buffers");
+  const int k8_src = 64 * (lane >> 2) + 16 * (((lane & 3) - 2 * ((lane >> 5) & 1)) & 3);
   auto fetch = [&](int step, int buf) {
     const int j = 4 * step + wave;
     const int id = bt[min(j, last_col)];
@@ -1373,12 +1445,14 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
         const int64_t off = (int64_t)id * blk_stride;
         const rsrc_t rk8 = run_rsrc8<D>(kbase + off, true);
         const rsrc_t rv8 = run_rsrc8<D>(vbase + off, true);
+        char* kdst = sm.bytes + (buf ? L8::kOff1 : L8::kOff0) + wave * L8::kRun;
+        char* vdst = sm.bytes + (buf ? L8::vOff1 : L8::vOff0) + wave * L8::vRun;
 #pragma unroll
-        for (int c = 0; c < kRun8 / 1024; ++c) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk8, (lds_void*)(stage_k + c * 1024), 16,
-                                                   16 * lane + 1024 * c, 0, 0,
+        for (int c = 0; c < D / 64; ++c) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk8, (lds_void*)(kdst + c * 1024), 16,
+                                                   k8_src + 1024 * c, 0, 0,
                                                    kPrefillLoadPolicy);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv8, (lds_void*)(stage_v + c * 1024), 16,
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv8, (lds_void*)(vdst + c * 1024), 16,
                                                    16 * lane + 1024 * c, 0, 0,
                                                    kPrefillLoadPolicy);
         }
@@ -1406,40 +1480,21 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
   // and zero V tokens past the context in the last block (their weight is 0,
   // but the pool may hold NaN there and 0 * NaN would poison the sum).
   auto finish = [&](int step, int buf, bool ok) {
-    if (KV8) {  // widen this wave's staged FP8 runs into 16-bit buffer 0
-      char* kdst = sm.bytes + Lay::kOff0 + wave * Lay::kRun;
-      char* vdst = sm.bytes + Lay::vOff0 + wave * Lay::vRun;
-      if (lane == 0) sm.valid[0][wave] = ok ? 1 : 0;
-      const int tok0 = step * kPrefillStep + wave * kBlock;
+    if (KV8) {
+      // FP8 V unit i holds tokens 4 (i / 16) .. + 3 (byte e of each word is
+      // token 4 (i / 16) + e)
+      char* vdst = sm.bytes + (buf ? L8::vOff1 : L8::vOff0) + wave * L8::vRun;
+      if (lane == 0) sm.valid[buf][wave] = ok ? 1 : 0;
+      const int tok0 = step * kPrefillStep + wave * kBlock + 4 * (lane >> 4);
+      if (!ok || tok0 + 4 > L) {
+        unsigned keep = 0u;
 #pragma unroll
-      for (int q = 0; q < KQ; ++q) {
-        if (!ok) break;
-        // K: token lane & 15, dims 8(4q + (lane >> 4)) .. + 7, in 64-dim
-        // slab q / 2 at byte 32 (q % 2) + 8 (lane >> 4) of the token's row
-        const u32x2 k8 = *reinterpret_cast<const u32x2*>(
-            stage_k + (q >> 1) * 1024 + (lane & 15) * 64 + 32 * (q & 1) + 8 * (lane >> 4));
-        *reinterpret_cast<u32x4*>(kdst + q * 1024 + 16 * lane) =
-            __builtin_bit_cast(u32x4, fp8x8_to_bf16(k8.x, k8.y));
-      }
-      // V: lane (m, u, p) = (lane >> 5, (lane >> 3) & 3, lane & 7) reads the
-      // 32 staged bytes of token group u and dims 64 m + 2p + {0, 1} + 16 k
-      // (k = 0..3) -- word k of each 16-byte half holds 4 tokens of one of
-      // them -- and writes bf16 slots 32 (4m + k) + 8u + p, so each 16-lane
-      // group stores 256 contiguous bytes.
-      if (lane < D / 2) {
-        const int m = lane >> 5, u = (lane >> 3) & 3, p = lane & 7;
-        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-        if (ok) {
-          lo = *reinterpret_cast<const u32x4*>(stage_v + (m * 4 + u) * 256 + p * 32);
-          hi = *reinterpret_cast<const u32x4*>(stage_v + (m * 4 + u) * 256 + p * 32 + 16);
-        }
-        const bool tail = ok && tok0 + kBlock > L;
+        for (int e = 0; e < 4; ++e) keep |= (ok && tok0 + e < L) ? (0xFFu << (8 * e)) : 0u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          u32x4 vv = {0u, 0u, 0u, 0u};
-          if (ok) vv = __builtin_bit_cast(u32x4, fp8x8_to_bf16(lo[k], hi[k]));
-          if (tail) vv = keep_below4(vv, tok0 + 4 * u, L);
-          *reinterpret_cast<u32x4*>(vdst + (32 * (4 * m + k) + 8 * u + p) * 16) = vv;
+        for (int c = 0; c < D / 64; ++c) {
+          u32x4* pv = reinterpret_cast<u32x4*>(vdst + c * 1024 + 16 * lane);
+          const u32x4 v = ok ? *pv : u32x4{0u, 0u, 0u, 0u};
+          *pv = u32x4{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
         }
       }
       return;
@@ -1470,6 +1525,12 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
   // 256 (g % 2) in each tile) and 2(g % 2) + 1 (128 bytes further).
   const int k_rd = (n >> 3) * Lay::kRun + (g * 16 + 8 * ((n >> 2) & 1) + (n & 3)) * 16;
   const int v_rd = (g >> 1) * Lay::vRun + (g & 1) * 256 + n * 8;
+  // FP8: K operand unit of tile 0 (token tb = 8 ((n / 4) % 2) + n % 4 of
+  // block n / 8, swizzled dims unit g), V units of token groups 2 (g % 2) and
+  // 2 (g % 2) + 1 of block g / 2
+  const int tb8 = 8 * ((n >> 2) & 1) + (n & 3);
+  const int k8_rd = (n >> 3) * L8::kRun + 16 * (4 * tb8 + ((g + 2 * ((n >> 2) & 1)) & 3));
+  const int v8_rd = (g >> 1) * L8::vRun + (g & 1) * 512 + 16 * n;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
                                                        0x3F803F80u});
 
@@ -1493,11 +1554,13 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
   }
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
-    const int buf = KV8 ? 0 : step & 1;
+    const int buf = step & 1;
     const bool ok_next = fetch(step + 1, buf ^ 1);
     if (step * kPrefillStep <= p_hi) {
-      const char* kb = sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + k_rd;
-      const char* vb = sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + v_rd;
+      const char* kb = KV8 ? sm.bytes + (buf ? L8::kOff1 : L8::kOff0) + k8_rd
+                           : sm.bytes + (buf ? Lay::kOff1 : Lay::kOff0) + k_rd;
+      const char* vb = KV8 ? sm.bytes + (buf ? L8::vOff1 : L8::vOff0) + v8_rd
+                           : sm.bytes + (buf ? Lay::vOff1 : Lay::vOff0) + v_rd;
       const unsigned vw = *reinterpret_cast<const unsigned*>(sm.valid[buf]);
       const unsigned valid = (vw & 1u) | ((vw >> 7) & 2u) | ((vw >> 14) & 4u) | ((vw >> 21) & 8u);
       const bool mask = (step * kPrefillStep + kPrefillStep - 1 > p_lo) || valid != 0xFu;
@@ -1505,10 +1568,10 @@ __device__ void run_prefill(const AttnArgs& a, int group, float c2, float vs, in
       // MFMAs of half 1 are issued next to the softmax of half 0, and the PV
       // MFMAs of half 0 next to the softmax of half 1, so each wave keeps its
       // matrix unit busy while its vector unit forms the weights.
-      prefill_step<D, NT>(o, lacc, mref, has_ref, qf, kb, vb, mask, valid, step, p_col, ones);
+      prefill_step<D, NT, KV8>(o, lacc, mref, has_ref, qf, kb, vb, mask, valid, step, p_col,
+                               ones);
     }
     wait_copies();
-    if (KV8) __syncthreads();  // the single 16-bit buffer is read by every wave
     finish(step + 1, buf ^ 1, ok_next);
     __syncthreads();
   }
