@@ -390,9 +390,10 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_reqs, int32_t num_tokens,
  * multiple of num_kv_heads, row strides too small, split_tokens not a
  * multiple of 32, scale not finite and positive); PKV_ERR_UNSUPPORTED
  * (head_dim not 64/128, block_size not 16, more than 16 q heads per kv head,
- * or a work list longer than 2^24 - 1 items: one item per (request, kv head,
- * context partition) plus the prompt tiles -- only reachable with tiny forced
- * partitions of very long contexts); PKV_ERR_WORKSPACE; PKV_ERR_LAUNCH.
+ * or more than 2^24 - 1 workgroups: one per (request, kv head, context
+ * partition), one per prompt tile and, when the batch may hold prompt tiles,
+ * one more per CU -- only reachable with tiny forced partitions of very long
+ * contexts); PKV_ERR_WORKSPACE; PKV_ERR_LAUNCH.
  */
 pkv_status pkv_paged_attention_varlen(
     const void* q, int64_t q_row_stride, const void* key_cache, const void* value_cache,

@@ -256,7 +256,7 @@ static pkv_status attention_call(
   if (!pkv::make_attn_plan(num_reqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                            max_query_len, max_seq_len, split_tokens, dtype, &plan))
     return PKV_ERR_INVALID_ARG;
-  if (plan.max_items > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;  // grid bound: one per item
+  if (plan.grid > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;  // one workgroup per item + helpers
   if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!query_start_loc || !seq_lens) return PKV_ERR_INVALID_ARG;
   const int32_t esz = dtype == PKV_BF16 ? 2 : 4;

@@ -53,6 +53,7 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPrefillItemsWord = 4;  // workspace header word: prefill items at the list head
+constexpr int kClaimWord = 32;        // workspace header words: prompt-tile ticket and finisher counts
 
 // Compute units of the current device, cached per device id.  Concurrent
 // first calls from several host threads may each query the device; they
@@ -438,6 +439,8 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     n_items[2] = (int32_t)batch_sum;
     const int64_t np = pre_units * H;
     n_items[kPrefillItemsWord] = (int32_t)(np < max_items ? np : max_items);
+    n_items[kClaimWord] = 0;
+    n_items[kClaimWord + 1] = 0;
   }
 }
 
@@ -1608,42 +1611,69 @@ union MainSmem {
 // wave's softmax VALU work overlaps the other's MFMAs, and a decode item's
 // start-up latency overlaps the other workgroup's loads.
 //
-// Prefill items (the head of the list) run on P resident workgroups, each
-// walking its share of the list; decode items are one workgroup each,
-// dispatched after them.  P = min(prefill items, `slots`) (two per CU) when
-// the batch is all prompt tiles, and min(prefill items, `slots_mixed`) (one
-// per CU) when decode items follow: each CU then runs one MFMA-bound prompt
-// tile beside HBM-bound decode items instead of finishing the prompt before
-// the decodes start.  On the 5000-token chunk the resident form is about 4 %
-// faster than one workgroup per tile; for decode items it was slower (a
-// whole-list resident form with a claim counter or a fixed share lost
-// 13-17 % on decode batches), so they keep the hardware dispatcher's
-// balancing.
+// Prefill items (the head of the list) run on P resident workgroups; decode
+// items are one workgroup each, dispatched after them, so the hardware
+// dispatcher balances them.  A batch of prompt tiles only has P = min(prefill
+// items, `slots`) (two per CU), each walking a fixed snake over the
+// longest-first list.  A batch with decode items too has P = min(prefill
+// items, `slots_mixed`) (one per CU), so each CU runs one MFMA-bound prompt
+// tile beside HBM-bound decode items, and the prompt tiles are shared out
+// dynamically: each resident workgroup takes its first item directly and
+// claims the next ones in list order from a counter in the workspace header,
+// and `slots_mixed` helper workgroups placed after the decode items claim
+// from the same counter once the dispatcher reaches them, i.e. as the decode
+// items drain.  Without them the decode items finished 0.3 ms before the
+// last prompt tiles on the 5000-token chunk + 200 decodes (FP8 pools), with
+// one prompt workgroup per CU for that whole time.  The counter's last
+// claimant zeroes it for the next run over the same list.  (A whole-list
+// claim form for prompt-only batches lost 3-16 %: 512 workgroups claiming at
+// once serialise on one counter.)
 template <int D, bool KV8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_main_kernel(
     AttnArgs a, int32_t group, float c2, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items, int32_t max_splits, float* __restrict__ ml,
-    float* __restrict__ opart, int32_t slots, int32_t slots_mixed) {
+    float* __restrict__ opart, int32_t slots, int32_t slots_mixed, int32_t* __restrict__ claim) {
   __shared__ MainSmem<D> sm;
+  __shared__ int next_idx[2];
   const int n = n_items[0];
   const int n_pre = n_items[kPrefillItemsWord];
   // FP8 pools: k_scale joins the softmax scale, v_scale the output
   const float c2k = KV8 ? c2 * *a.k_scale : c2;
   const float vs = KV8 ? *a.v_scale : 1.f;
-  const int P = min(n_pre, n > n_pre ? slots_mixed : slots);
+  const bool mixed = n > n_pre && n_pre > 0;
+  const int P = min(n_pre, mixed ? slots_mixed : slots);
+  const int n_dec = n - n_pre;
+  // helper workgroups after the decode items (as many as the grid holds)
+  const int Hh = mixed ? max(0, min(slots_mixed, (int)gridDim.x - P - n_dec)) : 0;
   const int b = blockIdx.x;
-  if (b < P) {
-    // prefill items: the first P workgroups stay resident and take items
-    // b, 2P - 1 - b, 2P + b, ... (a snake over the longest-first list)
-    for (int k = 0;; ++k) {
-      const int idx = k * P + ((k & 1) ? P - 1 - b : b);
-      if (idx >= n_pre) break;
+  if (b < P || (mixed && b >= P + n_dec && b < P + n_dec + Hh)) {
+    // Prompt-only launch: the first P workgroups stay resident and take
+    // items b, 2P - 1 - b, 2P + b, ... (a snake over the longest-first list).
+    // Launch with decode items: the P resident workgroups take item b, then
+    // claim items in list order from a counter; the helper workgroups, which
+    // the dispatcher starts once the decode items are all placed, claim too.
+    auto take = [&](int slot) {
+      if (threadIdx.x == 0) next_idx[slot] = P + atomicAdd(claim, 1);
+      __syncthreads();
+      return next_idx[slot];
+    };
+    int slot = 0;
+    int idx = b < P ? b : take(slot);
+    for (int k = 1; idx < n_pre; ++k) {
       const int4 it = items[idx];
       run_prefill<D, KV8>(a, group, c2k, vs, it.x, it.y, it.z, sm.pre);
       __syncthreads();
+      slot ^= 1;
+      idx = mixed ? take(slot) : k * P + ((k & 1) ? P - 1 - b : b);
+    }
+    // the last claimant leaves the counters zeroed for the next run
+    if (mixed && threadIdx.x == 0 && atomicAdd(claim + 1, 1) == P + Hh - 1) {
+      atomicExch(claim, 0);
+      atomicExch(claim + 1, 0);
     }
     return;
   }
+  if (b >= P + n_dec) return;
   const int idx = n_pre + (b - P);
   if (idx >= n) return;
   const int4 it = items[idx];
@@ -1839,9 +1869,10 @@ hipError_t launch_run_d(const AttnArgs& a, const AttnPlan& plan, void* workspace
   const float c2 = a.scale * kLog2e;
   hipError_t e = hipSuccess;
   if (plan.max_items > 0) {
-    hipLaunchKernelGGL((attn_main_kernel<D, KV8>), dim3((unsigned)plan.max_items), dim3(kThreads), 0,
-                       stream, a, plan.group, c2, items, n_items, plan.max_splits, ml, opart,
-                       2 * device_cu_count(), device_cu_count());
+    hipLaunchKernelGGL((attn_main_kernel<D, KV8>), dim3((unsigned)plan.grid),
+                       dim3(kThreads), 0, stream, a, plan.group, c2, items, n_items,
+                       plan.max_splits, ml, opart, 2 * device_cu_count(), device_cu_count(),
+                       reinterpret_cast<int32_t*>(ws) + kClaimWord);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1898,6 +1929,9 @@ bool make_attn_plan(int32_t num_reqs, int32_t num_tokens, int32_t num_q_heads,
       ((int64_t)num_tokens * g + kPrefillPairs - 1) / kPrefillPairs + prefill_reqs;
   p.max_items = (int64_t)num_kv_heads * ((int64_t)num_reqs * p.max_splits + prefill_tiles);
   if (num_tokens == 0) p.max_items = 0;
+  // one workgroup per item, plus one helper per CU for the prompt tiles of a
+  // batch that also holds decode items
+  p.grid = p.max_items + (p.max_items > 0 && prefill_reqs > 0 ? device_cu_count() : 0);
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 256;  // header: item count
   p.items_offset = off;

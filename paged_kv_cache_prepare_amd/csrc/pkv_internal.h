@@ -22,7 +22,8 @@ struct AttnPlan {
   int32_t group;          // q heads per kv head
   int32_t split_tokens;   // partition size of a decode context (multiple of 32)
   int32_t max_splits;     // partitions per decode context, upper bound
-  int64_t max_items;      // upper bound on work items (grid size of the main kernel)
+  int64_t max_items;      // upper bound on work items
+  int64_t grid;           // workgroups of the main kernel: max_items + prompt helpers
   size_t items_offset;    // byte offsets inside the workspace
   size_t ml_offset;
   size_t o_offset;

@@ -4,6 +4,7 @@ one-call pkv_paged_attention_varlen* on the same inputs (the same kernels over
 the same list), for 16-bit and FP8 pools; a new plan in the same workspace
 serves a new batch; the checked build rejects a run over a list made for
 another batch."""
+import numpy as np
 import pytest
 import torch
 
@@ -93,6 +94,49 @@ def test_replanning_the_workspace_for_a_new_batch():
                                     **kw)
         torch.cuda.synchronize()
         assert torch.equal(bits_view(run), bits_view(fused))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_runs_that_claim_prompt_tiles(fp8):
+    """A batch with more prompt tiles than the chip has CUs plus decode items:
+    the resident prompt workgroups claim tiles from a counter in the
+    workspace, together with helper workgroups placed after the decode
+    items, and the run that claims last zeroes the counter.  Four runs over
+    one plan must equal each other bit for bit (which workgroup computes a
+    tile does not change its result) and the oracle, and out is pre-filled
+    with NaN, so a tile that no run computed would show."""
+    nst = [2000, 1, 1, 1, 3, 1]
+    nct = [1500, 700, 3000, 90, 40, 1200]
+    wl = workloads.build("claims", nst, nct, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                         seed=77, device=device(), pool_slack=1.2)
+    if fp8:
+        wl = workloads.to_fp8(wl, 0.0125, 0.02)
+    G = wl.num_q_heads // wl.num_kv_heads
+    tiles = -(-nst[0] * G // 128) * wl.num_kv_heads
+    assert tiles > torch.cuda.get_device_properties(0).multi_processor_count
+    prep, bt, kc, vc, ks, vs = _write(wl)
+    ws = pkv.paged_attention_plan(prep["query_start_loc"], prep["seq_lens"],
+                                  num_tokens=wl.num_tokens, num_q_heads=32, num_kv_heads=8,
+                                  head_dim=128, max_query_len=wl.max_query_len,
+                                  max_seq_len=wl.max_seq_len)
+    kw = dict(max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, scale=wl.scale,
+              k_scale=ks, v_scale=vs)
+    outs = []
+    for k in range(4):
+        out = torch.full_like(wl.q, float("nan"))
+        pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
+                            planned=True, workspace=ws, out=out, **kw)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for k in range(1, 4):
+        assert torch.equal(bits_view(outs[k]), bits_view(outs[0])), f"run {k}"
+    T = wl.num_tokens
+    rows = np.array(sorted(set(range(0, T, 37)) | {T - 1} | set(range(nst[0], T))), np.int32)
+    _, _, _, ref = oracle_step(wl, rows=rows)
+    got = outs[0][torch.from_numpy(rows).long().to(device())]
+    assert torch.isfinite(outs[0].float()).all()
+    assert_attention_close(got, ref, wl.dtype, "claimed prompt tiles")
+    log(f"  {tiles} prompt tiles, 4 runs over one plan: identical, and equal to the oracle")
 
 
 def test_fp32_plan_is_a_no_op_and_run_works():
