@@ -53,7 +53,8 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPrefillItemsWord = 4;  // workspace header word: prefill items at the list head
-constexpr int kClaimWord = 32;        // workspace header words: prompt-tile ticket and finisher counts
+constexpr int kClaimWord = 32;        // workspace header words: prompt-tile tickets per XCD, finishers
+constexpr int kXcds = 8;              // XCDs: workgroup b runs on XCD b % 8
 
 // Compute units of the current device, cached per device id.  Concurrent
 // first calls from several host threads may each query the device; they
@@ -439,8 +440,8 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     n_items[2] = (int32_t)batch_sum;
     const int64_t np = pre_units * H;
     n_items[kPrefillItemsWord] = (int32_t)(np < max_items ? np : max_items);
-    n_items[kClaimWord] = 0;
-    n_items[kClaimWord + 1] = 0;
+#pragma unroll
+    for (int x = 0; x <= kXcds; ++x) n_items[kClaimWord + x] = 0;
   }
 }
 
@@ -1619,13 +1620,14 @@ union MainSmem {
 // items, `slots_mixed`) (one per CU), so each CU runs one MFMA-bound prompt
 // tile beside HBM-bound decode items, and the prompt tiles are shared out
 // dynamically: each resident workgroup takes its first item directly and
-// claims the next ones in list order from a counter in the workspace header,
-// and `slots_mixed` helper workgroups placed after the decode items claim
-// from the same counter once the dispatcher reaches them, i.e. as the decode
+// claims the next ones in list order from a counter in the workspace header
+// (one counter per XCD, over the items of that XCD's residue class), and
+// `slots_mixed` helper workgroups placed after the decode items claim from
+// the same counters once the dispatcher reaches them, i.e. as the decode
 // items drain.  Without them the decode items finished 0.3 ms before the
 // last prompt tiles on the 5000-token chunk + 200 decodes (FP8 pools), with
-// one prompt workgroup per CU for that whole time.  The counter's last
-// claimant zeroes it for the next run over the same list.  (A whole-list
+// one prompt workgroup per CU for that whole time.  The last claimant zeroes
+// the counters for the next run over the same list.  (A whole-list
 // claim form for prompt-only batches lost 3-16 %: 512 workgroups claiming at
 // once serialise on one counter.)
 template <int D, bool KV8>
@@ -1652,8 +1654,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Launch with decode items: the P resident workgroups take item b, then
     // claim items in list order from a counter; the helper workgroups, which
     // the dispatcher starts once the decode items are all placed, claim too.
+    // Claims stay on the workgroup's XCD: XCD x hands out the items past P
+    // whose index is x mod 8 (for 8 kv heads, the tiles of one head), so a
+    // head's K/V blocks keep being read through one L2.
+    const int x = b % kXcds;
+    const int first = P + (x - P % kXcds + kXcds) % kXcds;
     auto take = [&](int slot) {
-      if (threadIdx.x == 0) next_idx[slot] = P + atomicAdd(claim, 1);
+      if (threadIdx.x == 0) next_idx[slot] = first + kXcds * atomicAdd(claim + x, 1);
       __syncthreads();
       return next_idx[slot];
     };
@@ -1667,9 +1674,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       idx = mixed ? take(slot) : k * P + ((k & 1) ? P - 1 - b : b);
     }
     // the last claimant leaves the counters zeroed for the next run
-    if (mixed && threadIdx.x == 0 && atomicAdd(claim + 1, 1) == P + Hh - 1) {
-      atomicExch(claim, 0);
-      atomicExch(claim + 1, 0);
+    if (mixed && threadIdx.x == 0 && atomicAdd(claim + kXcds, 1) == P + Hh - 1) {
+#pragma unroll
+      for (int y = 0; y <= kXcds; ++y) atomicExch(claim + y, 0);
     }
     return;
   }
