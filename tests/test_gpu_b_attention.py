@@ -332,6 +332,39 @@ def test_attention_shared_prefix_beside_prompt_tiles(Hq, Hkv, d):
         assert_attention_close(out, ref, wl.dtype, f"shared prefix beside prompt, split {st}")
 
 
+# Shared prefixes among split decode contexts of equal length, where every
+# sharer's partitions have the same bounds:
+#  * requests 0-3: four sharers over two whole partitions (prefix 2048 tokens);
+#  * requests 4, 5: two sharers, one with two query rows, whose prefix (704
+#    tokens) ends inside the first partition;
+#  * requests 6-8: three sharers of one partition;
+#  * request 9 shares request 0's blocks with a different length;
+#  * requests 10, 11: unshared.
+GROUP_NST = [1, 1, 1, 1, 1, 2, 1, 1, 1, 1, 1, 1]
+GROUP_NCT = [2999, 2999, 2999, 2999, 1999, 1998, 1499, 1499, 1499, 2899, 2499, 700]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("prompt", [False, True])
+def test_attention_equal_length_sharers(kv, prompt):
+    nst, nct = list(GROUP_NST), list(GROUP_NCT)
+    if prompt:  # a prompt chunk in the same launch
+        nst.append(40)
+        nct.append(64)
+    wl = workloads.build(f"groups_{kv}_{prompt}", nst, nct, num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, seed=61, device=device(), pool_slack=1.2,
+                         shared_prefix_groups=[([0, 1, 2, 3, 9], 2048), ([4, 5], 704),
+                                               ([6, 7, 8], 1024)])
+    if kv == "fp8":
+        wl = workloads.to_fp8(wl, 0.05, 0.03)
+    _, _, _, ref = oracle_step(wl)
+    # 0: the library's partitions (about one item per CU); 1024: the same by
+    # hand; 64: many short partitions
+    for st in (0, 1024, 64):
+        _, _, _, out = gpu_step(wl, split_tokens=st)
+        assert_attention_close(out, ref, wl.dtype, f"equal-length sharers {kv} prompt={prompt} split {st}")
+
+
 def _shape_scores(wl, growth, seed):
     """Give every key of kv head h the direction u_h scaled by growth[r](pos),
     plus noise, and every query of that head's group u_h plus noise, so that a
