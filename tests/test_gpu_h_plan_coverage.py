@@ -10,8 +10,9 @@ multiset, with the units derived here from the batch in plain Python.  The
 batches put decode requests whose lengths fall into the same coarse length
 rank on both sides of a partition boundary (lengths 256 and 257 at a
 256-token partition), the case where ordering decode requests by length
-rank alone would drop a partition or duplicate one.  A few of the batches
-then run end to end with the output and workspace pre-filled with NaN and are
+rank alone would drop a partition or duplicate one; batches of more than
+1024 requests take the request-order path.  A few of the batches then run
+end to end with the output and workspace pre-filled with NaN and are
 compared with the oracle.
 
 The list layout read here is the implementation's: a 256-byte header whose
@@ -196,3 +197,39 @@ def test_colliding_batches_end_to_end(seed):
                          num_kv_heads=2, head_dim=64, seed=950 + seed, device=device(),
                          pool_slack=1.2)
     _run_nan_filled(wl, split)
+
+
+def _many_requests(rng, R, split):
+    """R requests: mostly single-token decodes of 17..600 tokens, some
+    multi-row decodes and a few prompt chunks."""
+    q_len = np.ones(R, np.int64)
+    kind = rng.random(R)
+    q_len[kind < 0.05] = rng.integers(2, 4, int((kind < 0.05).sum()))
+    q_len[kind > 0.99] = rng.integers(20, 90, int((kind > 0.99).sum()))
+    L = rng.integers(17, 600, R).astype(np.int64)
+    on_edge = rng.random(R) < 0.1  # lengths on a partition boundary, or one past it
+    L[on_edge] = rng.integers(1, 8, int(on_edge.sum())) * split + rng.integers(0, 2, int(on_edge.sum()))
+    L = np.maximum(L, q_len + 1)
+    return q_len, L
+
+
+@pytest.mark.parametrize("R", [1025, 2500])
+def test_lists_of_more_requests_than_one_ranking_holds(R):
+    """Batches above 1024 requests take the plan's request-order path, 1024
+    requests per scan: the list must still hold every unit once."""
+    rng = np.random.default_rng(R)
+    for split, (Hq, Hkv) in ((64, (8, 2)), (256, (32, 8)), (1024, (4, 4))):
+        q_len, L = _many_requests(rng, R, split)
+        qsl = np.concatenate([[0], np.cumsum(q_len)]).astype(np.int32)
+        plan_and_check(qsl, L.astype(np.int32), Hq, Hkv, 64, split, f"R={R} split {split}")
+
+
+def test_many_requests_end_to_end():
+    """1100 requests through prepare -> write -> attention (request-order
+    plan path), NaN-filled output and workspace, against the oracle."""
+    rng = np.random.default_rng(1100)
+    q_len, L = _many_requests(rng, 1100, 64)
+    wl = workloads.build("many_reqs", q_len.tolist(), (L - q_len).tolist(), num_q_heads=8,
+                         num_kv_heads=2, head_dim=64, seed=1101, device=device(),
+                         pool_slack=1.2)
+    _run_nan_filled(wl, 64)
