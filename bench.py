@@ -1,12 +1,12 @@
 """Benchmark of one step of the paged-attention hot path on one MI355X.
 
-A step is the whole hot path over one batch: prepare_inputs (flat-batch
-indices and slot mapping) -> kv_cache_write (this step's K/V rows into the
-block pool) -> the attention plan (the work list) -> the attention run (main
-kernel, and the split-KV reduce when a context is partitioned).  Plan then
-run is the same work as one paged_attention_varlen call.  Inputs are
-resident in HBM before timing; outputs, workspace and index buffers are
-preallocated, so a step allocates nothing.
+A step is the whole hot path over one batch: prepare_inputs_and_plan (the
+flat-batch indices, the slot mapping and the attention work list, in one
+launch) -> kv_cache_write (this step's K/V rows into the block pool) -> the
+attention run (main kernel, and the split-KV reduce when a context is
+partitioned).  Plan then run is the same work as one paged_attention_varlen
+call.  Inputs are resident in HBM before timing; outputs, workspace and index
+buffers are preallocated, so a step allocates nothing.
 
 Default workload: the mixed chunked-prefill step ("Building the Batch", "Why
 flatten": one 5,000-token prompt chunk with 3,000 tokens already computed,
@@ -657,16 +657,21 @@ def step_buffers(wl, split_tokens):
 
 
 def make_phases(wl, b, split_tokens):
-    """The step's calls: prepare_inputs, kv_cache_write, the attention plan and
-    the attention run (main + reduce) over that plan.  Plan followed by run is
-    the same work as one paged_attention_varlen call."""
+    """The step's calls: prepare_inputs_and_plan (index tensors and the
+    attention work list), kv_cache_write, and the attention run (main +
+    reduce) over that list.  Plan followed by run is the same work as one
+    paged_attention_varlen call."""
     import paged_kv_cache_prepare_amd as pkv
     prep = b["prep"]
     kc, vc = wl.key_cache, wl.value_cache
 
-    def prepare():
-        pkv.prepare_inputs(b["nst"], b["nct"], b["bt"], num_tokens=wl.num_tokens,
-                           block_size=wl.block_size, num_blocks=wl.num_blocks, out=prep)
+    def prepare_plan():
+        pkv.prepare_inputs_and_plan(b["nst"], b["nct"], b["bt"], num_tokens=wl.num_tokens,
+                                    block_size=wl.block_size, num_blocks=wl.num_blocks,
+                                    num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                                    head_dim=wl.head_dim, max_query_len=wl.max_query_len,
+                                    max_seq_len=wl.max_seq_len, dtype=wl.dtype,
+                                    split_tokens=split_tokens, workspace=b["ws"], out=prep)
 
     def write():
         if b["ks"] is None:
@@ -676,20 +681,13 @@ def make_phases(wl, b, split_tokens):
             pkv.kv_cache_write_fp8(wl.key, wl.value, kc, vc, prep["slot_mapping"], b["ks"],
                                    b["vs"], block_size=wl.block_size)
 
-    def plan():
-        pkv.paged_attention_plan(prep["query_start_loc"], prep["seq_lens"],
-                                 num_tokens=wl.num_tokens, num_q_heads=wl.num_q_heads,
-                                 num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
-                                 max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
-                                 dtype=wl.dtype, split_tokens=split_tokens, workspace=b["ws"])
-
     def run():
         pkv.paged_attention(wl.q, kc, vc, prep["query_start_loc"], prep["seq_lens"], b["bt"],
                             max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
                             scale=wl.scale, out=b["out"], split_tokens=split_tokens,
                             workspace=b["ws"], k_scale=b["ks"], v_scale=b["vs"], planned=True)
 
-    return prepare, write, plan, run
+    return prepare_plan, write, run
 
 
 def roofline_of(work, t_ms):
@@ -760,12 +758,11 @@ def main():
         scratch.fill_(1.0)
 
     b = step_buffers(wl, args.split_tokens)
-    prepare, write, plan, run = make_phases(wl, b, args.split_tokens)
+    prepare_plan, write, run = make_phases(wl, b, args.split_tokens)
 
     def step():
-        prepare()
+        prepare_plan()
         write()
-        plan()
         run()
 
     def events(n):
@@ -793,21 +790,19 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     step_ms = [e[0].elapsed_time(e[1]) for e in ev]
     # phase pass, same protocol: events between the calls
-    ph = [events(5) for _ in range(args.steps)]
+    ph = [events(4) for _ in range(args.steps)]
     for k in range(args.steps):
         flush()
         ph[k][0].record(stream)
-        prepare()
+        prepare_plan()
         ph[k][1].record(stream)
         write()
         ph[k][2].record(stream)
-        plan()
-        ph[k][3].record(stream)
         run()
-        ph[k][4].record(stream)
+        ph[k][3].record(stream)
     torch.cuda.synchronize(dev)
     phase_ms = {name: [e[i].elapsed_time(e[i + 1]) for e in ph]
-                for i, name in enumerate(("prepare", "kv_write", "plan", "run"))}
+                for i, name in enumerate(("prepare_and_plan", "kv_write", "run"))}
     # the decode rows and the prompt rows alone over the same pools: the
     # per-path fractions (same protocol, attention run only)
     sub_lines = {}
@@ -817,9 +812,8 @@ def main():
                 continue
             sw = workloads.select(full, reqs)
             sb = step_buffers(sw, args.split_tokens)
-            s_prep, _, s_plan, s_run = make_phases(sw, sb, args.split_tokens)
-            s_prep()
-            s_plan()
+            s_prep_plan, _, s_run = make_phases(sw, sb, args.split_tokens)
+            s_prep_plan()
             for _ in range(max(2, args.warmup // 2)):
                 flush()
                 s_run()

@@ -23,6 +23,9 @@
  *                              two halves: the work list once per batch,
  *                              then any number of calls over it (one per
  *                              model layer);
+ *   pkv_prepare_inputs_and_plan  pkv_prepare_inputs and
+ *                              pkv_paged_attention_plan of one step in a
+ *                              single launch;
  *   pkv_copy_blocks            whole-block copies in both pools (copy-on-write
  *                              of a shared block);
  *   pkv_zero_blocks            whole-block clears in both pools (freshly
@@ -470,6 +473,36 @@ pkv_status pkv_paged_attention_run(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     float scale, pkv_dtype dtype, const float* k_scale, const float* v_scale,
     int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_prepare_inputs_and_plan -- pkv_prepare_inputs followed by
+ * pkv_paged_attention_plan over the query_start_loc and seq_lens it writes,
+ * in one launch.  In "vLLM's Model Runner -- the Persistent Batch, in
+ * Source" ("The Forward Pass", "One method, four jobs") the model runner
+ * builds the step's input tensors and then its attention metadata inside
+ * one input-preparation block; here the attention metadata is the work
+ * list.  Two calls back to back pay a launch boundary that one launch does
+ * not.
+ * Arguments: those of pkv_prepare_inputs, then those of
+ * pkv_paged_attention_plan that are not outputs of the prepare half
+ * (max_query_len .. workspace_bytes).  Results: identical to the two calls:
+ * the same index tensors, and a work list in `workspace` that any
+ * pkv_paged_attention_run precondition accepts (the order of items of equal
+ * rank may differ between any two plans, as it may between two plan calls).
+ * With dtype PKV_F32, or an empty batch, only the prepare half runs and
+ * `workspace` is not touched.  The checked build (libpkv_checked.so) runs
+ * the two calls one after the other, each with its device-data checks.
+ * Errors: those of either call, checked on the host before anything is
+ * enqueued.
+ */
+pkv_status pkv_prepare_inputs_and_plan(
+    const int32_t* num_scheduled_tokens, const int32_t* num_computed_tokens,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens,
+    int32_t qsl_len, int32_t block_size, int64_t num_blocks, int32_t* req_indices,
+    int32_t* positions, int64_t* slot_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+    int32_t* logits_indices, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype, int32_t split_tokens,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_paged_attention_varlen_noalloc -- pkv_paged_attention_varlen for

@@ -6,8 +6,8 @@ The compute lives in ``libpkv.so`` (HIP kernels behind the C ABI declared in
 """
 from .binding import (PkvError, attention_workspace_bytes, copy_blocks, kv_cache_write,
                       kv_cache_write_fp8, load, paged_attention, paged_attention_plan,
-                      prepare_input_ids, prepare_inputs, zero_blocks)
+                      prepare_input_ids, prepare_inputs, prepare_inputs_and_plan, zero_blocks)
 
 __all__ = ["PkvError", "attention_workspace_bytes", "copy_blocks", "kv_cache_write",
            "kv_cache_write_fp8", "load", "paged_attention", "paged_attention_plan",
-           "prepare_input_ids", "prepare_inputs", "zero_blocks"]
+           "prepare_input_ids", "prepare_inputs", "prepare_inputs_and_plan", "zero_blocks"]

@@ -33,7 +33,7 @@ EXPORTS = ("pkv_status_string", "pkv_debug_checks_enabled", "pkv_debug_check_fla
            "pkv_prepare_inputs", "pkv_prepare_input_ids",
            "pkv_kv_cache_write", "pkv_kv_cache_write_fp8", "pkv_paged_attention_workspace_bytes",
            "pkv_paged_attention_varlen", "pkv_paged_attention_varlen_fp8",
-           "pkv_paged_attention_plan", "pkv_paged_attention_run",
+           "pkv_paged_attention_plan", "pkv_paged_attention_run", "pkv_prepare_inputs_and_plan",
            "pkv_paged_attention_varlen_noalloc", "pkv_copy_blocks", "pkv_zero_blocks")
 
 
@@ -90,6 +90,10 @@ def load() -> ctypes.CDLL:
     lib.pkv_paged_attention_plan.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int,
                                              i32, P, sz, P]
     lib.pkv_paged_attention_plan.restype = ctypes.c_int
+    lib.pkv_prepare_inputs_and_plan.argtypes = [P, P, P, i64, i32, i32, i32, i32, i64, P, P, P, P,
+                                                P, P, i32, i32, i32, i32, i32, ctypes.c_int, i32,
+                                                P, sz, P]
+    lib.pkv_prepare_inputs_and_plan.restype = ctypes.c_int
     lib.pkv_paged_attention_run.argtypes = [P, i64, P, P, i64, P, i64, P, P, P, i64, i32, i32, i32,
                                             i32, i32, i32, i32, i32, f32, ctypes.c_int, P, P, i32,
                                             P, sz, P]
@@ -177,6 +181,48 @@ def prepare_inputs(num_scheduled_tokens: torch.Tensor, num_computed_tokens: torc
         _stream(dev))
     _check(st, "pkv_prepare_inputs")
     return out
+
+
+def prepare_inputs_and_plan(num_scheduled_tokens: torch.Tensor, num_computed_tokens: torch.Tensor,
+                            block_table: torch.Tensor, *, num_tokens: int, block_size: int,
+                            num_blocks: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            max_query_len: int, max_seq_len: int,
+                            dtype: torch.dtype = torch.bfloat16, split_tokens: int = 0,
+                            workspace: torch.Tensor | None = None, qsl_len: int | None = None,
+                            out: dict | None = None) -> tuple[dict, torch.Tensor]:
+    """pkv_prepare_inputs_and_plan: prepare_inputs and paged_attention_plan of
+    one step in one launch.  Returns (the prepare outputs, the workspace that
+    holds the work list); arguments as for the two calls."""
+    R = int(num_scheduled_tokens.shape[0])
+    dev = num_scheduled_tokens.device
+    qsl_len = R + 1 if qsl_len is None else int(qsl_len)
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {"req_indices": torch.empty(num_tokens, **i32),
+               "positions": torch.empty(num_tokens, **i32),
+               "slot_mapping": torch.empty(num_tokens, dtype=torch.int64, device=dev),
+               "query_start_loc": torch.empty(qsl_len, **i32),
+               "seq_lens": torch.empty(R, **i32),
+               "logits_indices": torch.empty(R, **i32)}
+    split_tokens = split_tokens_or_env(split_tokens)
+    need = attention_workspace_bytes(R, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                     max_query_len, max_seq_len, split_tokens, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    assert block_table.dim() == 2 and (block_table.numel() == 0 or block_table.stride(1) == 1)
+    st = load().pkv_prepare_inputs_and_plan(
+        _dev(num_scheduled_tokens, torch.int32, "num_scheduled_tokens"),
+        _dev(num_computed_tokens, torch.int32, "num_computed_tokens"),
+        _dev(block_table, torch.int32, "block_table"), max(1, block_table.stride(0)), R,
+        int(num_tokens), qsl_len, int(block_size), int(num_blocks),
+        _dev(out["req_indices"], torch.int32), _dev(out["positions"], torch.int32),
+        _dev(out["slot_mapping"], torch.int64), _dev(out["query_start_loc"], torch.int32),
+        _dev(out["seq_lens"], torch.int32), _dev(out["logits_indices"], torch.int32),
+        int(max_query_len), int(max_seq_len), int(num_q_heads), int(num_kv_heads),
+        int(head_dim), _dtype_code(dtype), int(split_tokens), _dev(workspace, name="workspace"),
+        workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "pkv_prepare_inputs_and_plan")
+    return out, workspace
 
 
 def prepare_input_ids(token_table: torch.Tensor, req_indices: torch.Tensor,

@@ -67,13 +67,18 @@ uint32_t pkv_debug_check_flags(void) {
 #endif
 }
 
-pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
-                              const int32_t* num_computed_tokens, const int32_t* block_table,
-                              int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens,
-                              int32_t qsl_len, int32_t block_size, int64_t num_blocks,
-                              int32_t* req_indices, int32_t* positions, int64_t* slot_mapping,
-                              int32_t* query_start_loc, int32_t* seq_lens,
-                              int32_t* logits_indices, void* stream) {
+}  // extern "C"
+
+// Host checks of pkv_prepare_inputs' arguments.
+static pkv_status prepare_args_status(const int32_t* num_scheduled_tokens,
+                                      const int32_t* num_computed_tokens,
+                                      const int32_t* block_table, int64_t bt_row_stride,
+                                      int32_t num_reqs, int32_t num_tokens, int32_t qsl_len,
+                                      int32_t block_size, int64_t num_blocks,
+                                      const int32_t* req_indices, const int32_t* positions,
+                                      const int64_t* slot_mapping,
+                                      const int32_t* query_start_loc, const int32_t* seq_lens,
+                                      const int32_t* logits_indices) {
   if (num_reqs < 0 || num_tokens < 0 || qsl_len < num_reqs + 1 || block_size < 1 ||
       num_blocks < 0)
     return PKV_ERR_INVALID_ARG;
@@ -84,6 +89,23 @@ pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
   if (num_tokens > 0 && (num_reqs == 0 || !block_table || bt_row_stride < 1 || !req_indices ||
                          !positions || !slot_mapping))
     return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+extern "C" {
+
+pkv_status pkv_prepare_inputs(const int32_t* num_scheduled_tokens,
+                              const int32_t* num_computed_tokens, const int32_t* block_table,
+                              int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens,
+                              int32_t qsl_len, int32_t block_size, int64_t num_blocks,
+                              int32_t* req_indices, int32_t* positions, int64_t* slot_mapping,
+                              int32_t* query_start_loc, int32_t* seq_lens,
+                              int32_t* logits_indices, void* stream) {
+  const pkv_status st = prepare_args_status(
+      num_scheduled_tokens, num_computed_tokens, block_table, bt_row_stride, num_reqs,
+      num_tokens, qsl_len, block_size, num_blocks, req_indices, positions, slot_mapping,
+      query_start_loc, seq_lens, logits_indices);
+  if (st != PKV_OK) return st;
   PKV_CHECK(pkv::check_prepare(num_scheduled_tokens, num_computed_tokens, block_table,
                                bt_row_stride, num_reqs, num_tokens, block_size, num_blocks,
                                static_cast<hipStream_t>(stream)));
@@ -230,17 +252,13 @@ static uint32_t plan_fingerprint(const pkv::AttnPlan& plan, int32_t num_reqs, in
   return h;
 }
 
-static pkv_status attention_call(
-    AttnMode mode, const void* q, int64_t q_row_stride, const void* key_cache,
-    const void* value_cache, int64_t num_blocks, void* out, int64_t out_row_stride,
-    const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* block_table,
-    int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens, int32_t max_query_len,
-    int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t block_size, float scale, pkv_dtype dtype, const float* k_scale,
-    const float* v_scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
-    void* stream) {
-  const bool kv8 = k_scale != nullptr;
-  const bool runs = mode != AttnMode::kPlan;
+// Host checks of an attention call's sizes and its work-list plan (every
+// attention entry point; `runs` for the calls that run the kernels).
+static pkv_status attention_plan_for(bool runs, int32_t num_reqs, int32_t num_tokens,
+                                     int32_t max_query_len, int32_t max_seq_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, float scale, pkv_dtype dtype,
+                                     int32_t split_tokens, pkv::AttnPlan* plan) {
   if (num_reqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0 ||
       num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
       split_tokens < 0 || split_tokens % 32 != 0)
@@ -252,11 +270,36 @@ static pkv_status attention_call(
   const int32_t group = num_q_heads / num_kv_heads;
   if (dtype == PKV_BF16 && group > pkv::kPairsPerTile) return PKV_ERR_UNSUPPORTED;
   if (num_q_heads > 65535) return PKV_ERR_UNSUPPORTED;
-  pkv::AttnPlan plan;
   if (!pkv::make_attn_plan(num_reqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
-                           max_query_len, max_seq_len, split_tokens, dtype, &plan))
+                           max_query_len, max_seq_len, split_tokens, dtype, plan))
     return PKV_ERR_INVALID_ARG;
-  if (plan.grid > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;  // one workgroup per item + helpers
+  if (plan->grid > kMaxWorkgroups) return PKV_ERR_UNSUPPORTED;  // one workgroup per item + helpers
+  return PKV_OK;
+}
+
+static bool workspace_fits(const pkv::AttnPlan& plan, const void* workspace,
+                           size_t workspace_bytes) {
+  return plan.total_bytes == 0 ||
+         (workspace != nullptr && workspace_bytes >= plan.total_bytes &&
+          (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0);
+}
+
+static pkv_status attention_call(
+    AttnMode mode, const void* q, int64_t q_row_stride, const void* key_cache,
+    const void* value_cache, int64_t num_blocks, void* out, int64_t out_row_stride,
+    const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* block_table,
+    int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens, int32_t max_query_len,
+    int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, pkv_dtype dtype, const float* k_scale,
+    const float* v_scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  const bool kv8 = k_scale != nullptr;
+  const bool runs = mode != AttnMode::kPlan;
+  pkv::AttnPlan plan;
+  const pkv_status st =
+      attention_plan_for(runs, num_reqs, num_tokens, max_query_len, max_seq_len, num_q_heads,
+                         num_kv_heads, head_dim, block_size, scale, dtype, split_tokens, &plan);
+  if (st != PKV_OK) return st;
   if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!query_start_loc || !seq_lens) return PKV_ERR_INVALID_ARG;
   const int32_t esz = dtype == PKV_BF16 ? 2 : 4;
@@ -272,10 +315,7 @@ static pkv_status attention_call(
         q_row_stride * esz % 16 != 0 || out_row_stride * esz % 16 != 0)
       return PKV_ERR_INVALID_ARG;
   }
-  if (plan.total_bytes > 0 &&
-      (workspace == nullptr || workspace_bytes < plan.total_bytes ||
-       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
-    return PKV_ERR_WORKSPACE;
+  if (!workspace_fits(plan, workspace, workspace_bytes)) return PKV_ERR_WORKSPACE;
 
   pkv::AttnArgs a;
   a.q = q;
@@ -364,6 +404,57 @@ pkv_status pkv_paged_attention_plan(const int32_t* query_start_loc, const int32_
                         max_query_len, max_seq_len, num_q_heads, num_kv_heads, head_dim,
                         pkv::kBlock, 1.f, dtype, nullptr, nullptr, split_tokens, workspace,
                         workspace_bytes, stream);
+}
+
+pkv_status pkv_prepare_inputs_and_plan(
+    const int32_t* num_scheduled_tokens, const int32_t* num_computed_tokens,
+    const int32_t* block_table, int64_t bt_row_stride, int32_t num_reqs, int32_t num_tokens,
+    int32_t qsl_len, int32_t block_size, int64_t num_blocks, int32_t* req_indices,
+    int32_t* positions, int64_t* slot_mapping, int32_t* query_start_loc, int32_t* seq_lens,
+    int32_t* logits_indices, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype, int32_t split_tokens,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = prepare_args_status(
+      num_scheduled_tokens, num_computed_tokens, block_table, bt_row_stride, num_reqs,
+      num_tokens, qsl_len, block_size, num_blocks, req_indices, positions, slot_mapping,
+      query_start_loc, seq_lens, logits_indices);
+  if (st != PKV_OK) return st;
+  pkv::AttnPlan plan;
+  st = attention_plan_for(false, num_reqs, num_tokens, max_query_len, max_seq_len, num_q_heads,
+                          num_kv_heads, head_dim, pkv::kBlock, 1.f, dtype, split_tokens, &plan);
+  if (st != PKV_OK) return st;
+  // a work list exists for bf16 queries and a non-empty batch (as for
+  // pkv_paged_attention_plan, which leaves the workspace alone otherwise)
+  const bool listed = dtype == PKV_BF16 && num_tokens > 0 && num_reqs > 0;
+  if (listed && !workspace_fits(plan, workspace, workspace_bytes)) return PKV_ERR_WORKSPACE;
+#ifdef PKV_DEBUG_CHECKS
+  // the checked build validates the prepare inputs, then the plan's inputs
+  // on the device, so it runs the two calls one after the other
+  st = pkv_prepare_inputs(num_scheduled_tokens, num_computed_tokens, block_table,
+                          bt_row_stride, num_reqs, num_tokens, qsl_len, block_size, num_blocks,
+                          req_indices, positions, slot_mapping, query_start_loc, seq_lens,
+                          logits_indices, stream);
+  if (st != PKV_OK || !listed) return st;
+  return pkv_paged_attention_plan(query_start_loc, seq_lens, num_reqs, num_tokens,
+                                  max_query_len, max_seq_len, num_q_heads, num_kv_heads,
+                                  head_dim, dtype, split_tokens, workspace, workspace_bytes,
+                                  stream);
+#else
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!listed)
+    return launch_status(pkv::launch_prepare(
+        num_scheduled_tokens, num_computed_tokens, block_table, bt_row_stride, num_reqs,
+        num_tokens, qsl_len, block_size, num_blocks, req_indices, positions, slot_mapping,
+        query_start_loc, seq_lens, logits_indices, s));
+  const pkv::PrepareArgs p = {num_scheduled_tokens, num_computed_tokens, block_table,
+                              bt_row_stride,        num_reqs,            num_tokens,
+                              qsl_len,              block_size,          num_blocks,
+                              req_indices,          positions,           slot_mapping,
+                              query_start_loc,      seq_lens,            logits_indices};
+  const uint32_t fp = plan_fingerprint(plan, num_reqs, num_tokens, max_query_len, max_seq_len,
+                                       num_q_heads, num_kv_heads, head_dim);
+  return launch_status(pkv::launch_prepare_plan(p, plan, num_kv_heads, workspace, fp, s));
+#endif
 }
 
 pkv_status pkv_paged_attention_run(

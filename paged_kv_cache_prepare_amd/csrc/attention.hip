@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "pkv_internal.h"
+#include "prepare_rows.h"
 
 namespace pkv {
 namespace {
@@ -245,8 +246,11 @@ __device__ inline int plan_units(const int32_t* qsl, const int32_t* seq_lens, in
 // later partitions of a context are its shorter remainders, and requests that
 // share prefix blocks read those blocks at about the same time.
 // Chunked path (larger batches): request order, 1024 requests per scan.
-__global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
-    const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t num_reqs,
+// The list is built by one 1024-thread workgroup: the plan kernel, or
+// workgroup 0 of the fused prepare + plan kernel once it has written
+// query_start_loc and seq_lens.
+__device__ __attribute__((always_inline)) inline void plan_body(
+    const int32_t* qsl, const int32_t* seq_lens, int32_t num_reqs,
     int32_t num_tokens, int32_t num_kv_heads, int32_t group, int32_t split_tokens, int32_t max_splits,
     int64_t max_items, int4* __restrict__ items, int32_t* __restrict__ n_items,
     uint32_t fingerprint) {
@@ -442,6 +446,48 @@ __global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
     n_items[kPrefillItemsWord] = (int32_t)(np < max_items ? np : max_items);
 #pragma unroll
     for (int x = 0; x <= kXcds; ++x) n_items[kClaimWord + x] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kPlanReqs) void attn_plan_kernel(
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t num_reqs,
+    int32_t num_tokens, int32_t num_kv_heads, int32_t group, int32_t split_tokens, int32_t max_splits,
+    int64_t max_items, int4* __restrict__ items, int32_t* __restrict__ n_items,
+    uint32_t fingerprint) {
+  plan_body(qsl, seq_lens, num_reqs, num_tokens, num_kv_heads, group, split_tokens, max_splits,
+            max_items, items, n_items, fingerprint);
+}
+
+// The step's index tensors and its attention work list in one launch (the
+// two are computed by the same step, and a launch boundary between them
+// costs more than either): workgroup 0 writes the per-request outputs
+// (query_start_loc, seq_lens, logits_indices, the padded tail), then builds
+// the work list from them; workgroups 1, 2, ... map 1024 flat rows each.
+// The per-request outputs are read back by the workgroup that wrote them,
+// after a barrier.
+__global__ __launch_bounds__(kPlanReqs) void prepare_plan_kernel(
+    const int32_t* __restrict__ nst, const int32_t* __restrict__ nct,
+    const int32_t* __restrict__ block_table, int64_t bt_stride, int32_t num_reqs,
+    int32_t num_tokens, int32_t qsl_len, int32_t block_size, int64_t num_blocks,
+    int32_t* __restrict__ req_indices, int32_t* __restrict__ positions,
+    int64_t* __restrict__ slot_mapping, int32_t* qsl, int32_t* seq_lens,
+    int32_t* __restrict__ logits_indices, int32_t num_kv_heads, int32_t group,
+    int32_t split_tokens, int32_t max_splits, int64_t max_items, int4* __restrict__ items,
+    int32_t* __restrict__ n_items, uint32_t fingerprint) {
+  if (blockIdx.x == 0) {
+    prepare_rows<kPlanReqs>(nst, nct, block_table, bt_stride, num_reqs, num_tokens, qsl_len,
+                            block_size, num_blocks, req_indices, positions, slot_mapping, qsl,
+                            seq_lens, logits_indices, 0, 0, true);
+    __syncthreads();
+    if (num_tokens > 0 && num_reqs > 0 && items != nullptr)
+      plan_body(qsl, seq_lens, num_reqs, num_tokens, num_kv_heads, group, split_tokens,
+                max_splits, max_items, items, n_items, fingerprint);
+  } else {
+    const int64_t row_lo = (int64_t)(blockIdx.x - 1) * kPlanReqs;
+    prepare_rows<kPlanReqs>(nst, nct, block_table, bt_stride, num_reqs, num_tokens, qsl_len,
+                            block_size, num_blocks, req_indices, positions, slot_mapping, qsl,
+                            seq_lens, logits_indices, row_lo,
+                            min((int64_t)num_tokens, row_lo + kPlanReqs), false);
   }
 }
 
@@ -1865,6 +1911,24 @@ hipError_t launch_plan(const AttnArgs& a, const AttnPlan& plan, void* workspace,
   return hipGetLastError();
 }
 
+// prepare_plan_kernel: 1 + ceil(num_tokens / 1024) workgroups.  A plan
+// without a work list (no tokens, no requests, or the fp32 path) leaves the
+// workspace alone.
+hipError_t launch_prepare_plan_k(const PrepareArgs& p, const AttnPlan& plan, int32_t num_kv_heads,
+                                 void* workspace, uint32_t fingerprint, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const bool listed = plan.max_items > 0 && p.num_tokens > 0 && p.num_reqs > 0 && ws != nullptr;
+  const int groups = 1 + (p.num_tokens + kPlanReqs - 1) / kPlanReqs;
+  hipLaunchKernelGGL(prepare_plan_kernel, dim3(groups), dim3(kPlanReqs), 0, stream, p.nst, p.nct,
+                     p.block_table, p.bt_stride, p.num_reqs, p.num_tokens, p.qsl_len,
+                     p.block_size, p.num_blocks, p.req_indices, p.positions, p.slot_mapping,
+                     p.qsl, p.seq_lens, p.logits_indices, num_kv_heads, plan.group,
+                     plan.split_tokens, plan.max_splits, plan.max_items,
+                     listed ? reinterpret_cast<int4*>(ws + plan.items_offset) : nullptr,
+                     listed ? reinterpret_cast<int32_t*>(ws) : nullptr, fingerprint);
+  return hipGetLastError();
+}
+
 template <int D, bool KV8>
 hipError_t launch_run_d(const AttnArgs& a, const AttnPlan& plan, void* workspace,
                         hipStream_t stream) {
@@ -1959,6 +2023,11 @@ hipError_t launch_attention_plan(const AttnArgs& a, const AttnPlan& plan, void* 
                                  uint32_t fingerprint, hipStream_t stream) {
   if (a.num_tokens == 0 || a.num_reqs == 0) return hipSuccess;
   return launch_plan(a, plan, workspace, fingerprint, stream);
+}
+
+hipError_t launch_prepare_plan(const PrepareArgs& p, const AttnPlan& plan, int32_t num_kv_heads,
+                               void* workspace, uint32_t fingerprint, hipStream_t stream) {
+  return launch_prepare_plan_k(p, plan, num_kv_heads, workspace, fingerprint, stream);
 }
 
 hipError_t launch_attention_run(const AttnArgs& a, const AttnPlan& plan, void* workspace,

@@ -69,6 +69,25 @@ hipError_t launch_prepare(const int32_t* nst, const int32_t* nct, const int32_t*
                           int32_t* qsl, int32_t* seq_lens, int32_t* logits_indices,
                           hipStream_t stream);
 
+// The arguments of pkv_prepare_inputs.
+struct PrepareArgs {
+  const int32_t* nst;
+  const int32_t* nct;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int32_t num_reqs;
+  int32_t num_tokens;
+  int32_t qsl_len;
+  int32_t block_size;
+  int64_t num_blocks;
+  int32_t* req_indices;
+  int32_t* positions;
+  int64_t* slot_mapping;
+  int32_t* qsl;
+  int32_t* seq_lens;
+  int32_t* logits_indices;
+};
+
 hipError_t launch_input_ids(const int32_t* token_table, int64_t row_width, int32_t num_reqs,
                             const int32_t* req_indices, const int32_t* positions,
                             int32_t num_tokens, const int32_t* seq_lens,
@@ -128,6 +147,10 @@ hipError_t launch_attention_plan(const AttnArgs& a, const AttnPlan& plan, void* 
                                  uint32_t fingerprint, hipStream_t stream);
 hipError_t launch_attention_run(const AttnArgs& a, const AttnPlan& plan, void* workspace,
                                 bool kv8, hipStream_t stream);
+// prepare (p) and the bf16 work list (plan) of the same step in one launch;
+// the list is read from the query_start_loc / seq_lens that p writes.
+hipError_t launch_prepare_plan(const PrepareArgs& p, const AttnPlan& plan, int32_t num_kv_heads,
+                               void* workspace, uint32_t fingerprint, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -70,6 +70,29 @@ def test_prepare_checks(checked):
     _fails("block_id", pkv.prepare_inputs, _i32([1, 5, 1]), nct, narrow, num_tokens=7, **kw)
 
 
+def test_fused_prepare_and_plan_checks(checked):
+    """The checked build runs pkv_prepare_inputs_and_plan as its two calls,
+    each with its device-data checks: bad prepare inputs fail before the plan,
+    and valid ones give the regular build's index tensors and list header."""
+    wl = _small()
+    bt = torch.from_numpy(wl.block_table).to(device())
+    nct = torch.from_numpy(wl.num_computed_tokens).to(device())
+    kw = dict(block_size=16, num_blocks=wl.num_blocks, num_q_heads=8, num_kv_heads=2,
+              head_dim=128, max_query_len=5, max_seq_len=301, split_tokens=64)
+    _fails("counts", pkv.prepare_inputs_and_plan, _i32([1, -5, 1]), nct, bt, num_tokens=7, **kw)
+    bad = bt.clone()
+    bad[2, 300 // 16] = wl.num_blocks + 4
+    _fails("block_id", pkv.prepare_inputs_and_plan, _i32([1, 5, 1]), nct, bad, num_tokens=7, **kw)
+    got, ws = pkv.prepare_inputs_and_plan(_i32([1, 5, 1]), nct, bt, num_tokens=7, **kw)
+    binding.use_checked(False)
+    ref, ws_ref = pkv.prepare_inputs_and_plan(_i32([1, 5, 1]), nct, bt, num_tokens=7, **kw)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
+    words = [0, 1, 2, 4]
+    assert ws[:256].view(torch.int32)[words].tolist() == ws_ref[:256].view(torch.int32)[words].tolist()
+
+
 def test_write_checks(checked):
     wl = _small()
     kc, vc = wl.key_cache.clone(), wl.value_cache.clone()

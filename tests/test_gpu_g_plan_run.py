@@ -184,3 +184,87 @@ def test_checked_build_rejects_a_stale_plan():
         torch.cuda.synchronize()
     finally:
         binding.use_checked(False)
+
+
+# pkv_prepare_inputs_and_plan: prepare + plan of one step in one launch.
+FUSED = {
+    # name: (nst, nct, Hq, Hkv, dtype, split, host token count (None: exact))
+    "mixed": (NST, NCT, 16, 4, torch.bfloat16, 0, None),
+    "mixed_split64": (NST, NCT, 16, 4, torch.bfloat16, 64, None),
+    "decodes": ([1] * 40, [100 + 37 * i for i in range(40)], 32, 8, torch.bfloat16, 0, None),
+    "padded": ([2, 5, 3], [14, 0, 9], 8, 2, torch.bfloat16, 0, 13),
+    "f32": ([2, 5, 3], [14, 0, 9], 4, 2, torch.float32, 0, None),
+    "many": (None, None, 8, 2, torch.bfloat16, 64, None),
+}
+
+
+def _list_of(ws):
+    w = ws.cpu()
+    head = w[:256].view(torch.int32).numpy().copy()
+    n = int(head[0])
+    items = w[256:256 + 16 * n].view(torch.int32).numpy().reshape(n, 4)
+    return head, sorted(map(tuple, items.tolist()))
+
+
+@pytest.mark.parametrize("case", list(FUSED))
+def test_prepare_and_plan_in_one_launch(case):
+    """The fused call writes the index tensors of pkv_prepare_inputs bit for
+    bit, and a work list with the same header words (item counts, record of
+    the sizes, batch checksum, zeroed claim counters) and the same items, as
+    a multiset, as pkv_paged_attention_plan over those tensors.  Attention
+    over the fused list matches the oracle."""
+    nst, nct, Hq, Hkv, dtype, split, host_T = FUSED[case]
+    if case == "many":  # more requests than one ranking pass of the plan holds
+        rng = np.random.default_rng(77)
+        nst = [1] * 1100
+        nst[5] = 40
+        nct = rng.integers(16, 300, 1100).tolist()
+    wl = workloads.build(f"fused_{case}", nst, nct, num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=128 if dtype == torch.bfloat16 else 64, dtype=dtype,
+                         seed=500 + len(case), device=device(), pool_slack=1.2)
+    dev = wl.q.device
+    T = wl.num_tokens if host_T is None else host_T
+    args = (torch.from_numpy(wl.num_scheduled_tokens).to(dev),
+            torch.from_numpy(wl.num_computed_tokens).to(dev),
+            torch.from_numpy(wl.block_table).to(dev))
+    sizes = dict(num_q_heads=Hq, num_kv_heads=Hkv, head_dim=wl.head_dim,
+                 max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len, dtype=dtype,
+                 split_tokens=split)
+    need = pkv.attention_workspace_bytes(wl.num_reqs, T, Hq, Hkv, wl.head_dim, wl.max_query_len,
+                                         wl.max_seq_len, split, dtype)
+    ws_a = torch.full((max(need, 256),), 0xFF, dtype=torch.uint8, device=dev)
+    ws_b = ws_a.clone()
+    prep_a = pkv.prepare_inputs(*args, num_tokens=T, block_size=16, num_blocks=wl.num_blocks,
+                                qsl_len=wl.num_reqs + 3)
+    pkv.paged_attention_plan(prep_a["query_start_loc"][:wl.num_reqs + 1], prep_a["seq_lens"],
+                             num_tokens=T, workspace=ws_a, **sizes)
+    prep_b, ws = pkv.prepare_inputs_and_plan(*args, num_tokens=T, block_size=16,
+                                             num_blocks=wl.num_blocks, workspace=ws_b,
+                                             qsl_len=wl.num_reqs + 3, **sizes)
+    torch.cuda.synchronize()
+    assert ws is ws_b
+    for k in prep_a:
+        assert torch.equal(prep_a[k], prep_b[k]), f"{case}: {k} differs"
+    if dtype != torch.bfloat16:
+        assert bool((ws_b == 0xFF).all()), f"{case}: the fp32 path wrote the workspace"
+        return
+    head_a, items_a = _list_of(ws_a)
+    head_b, items_b = _list_of(ws_b)
+    words = [0, 1, 2, 4] + list(range(32, 41))
+    assert head_a[words].tolist() == head_b[words].tolist(), f"{case}: list header differs"
+    assert items_a == items_b, f"{case}: list items differ"
+    assert head_b[0] > 0
+    if case in ("many", "padded"):
+        # the request-order list itself is checked by the plan coverage tests;
+        # a run must use the plan's token count, which for "padded" is not q's
+        return
+    kc, vc = wl.key_cache.clone(), wl.value_cache.clone()
+    pkv.kv_cache_write(wl.key, wl.value, kc, vc, prep_b["slot_mapping"], block_size=16)
+    out = torch.full_like(wl.q, float("nan"))
+    pkv.paged_attention(wl.q, kc, vc, prep_b["query_start_loc"][:wl.num_reqs + 1],
+                        prep_b["seq_lens"], args[2], max_query_len=wl.max_query_len,
+                        max_seq_len=wl.max_seq_len, scale=wl.scale, out=out,
+                        split_tokens=split, workspace=ws_b, planned=True)
+    torch.cuda.synchronize()
+    _, _, _, ref = oracle_step(wl)
+    assert_attention_close(out, ref, wl.dtype, f"fused {case}")
