@@ -28,7 +28,11 @@ def _buffers(wl, dev):
     return prep, ws
 
 
-def test_step_replays_in_a_hip_graph():
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_replays_in_a_hip_graph(fused):
+    """fused: the step as the benchmark runs it, prepare and the work list in
+    one launch (pkv_prepare_inputs_and_plan), then the write and a run over
+    the list."""
     dev = device()
     # decodes that are split into partitions, a prompt chunk, a short multi-row decode
     wl = workloads.build("graph", [1, 1, 70, 3, 1], [900, 40, 100, 20, 2000], num_q_heads=16,
@@ -43,12 +47,21 @@ def test_step_replays_in_a_hip_graph():
     prep, ws = _buffers(wl, dev)
 
     def step():
-        pkv.prepare_inputs(nst, nct, bt, num_tokens=wl.num_tokens, block_size=wl.block_size,
-                           num_blocks=wl.num_blocks, out=prep)
+        if fused:
+            pkv.prepare_inputs_and_plan(nst, nct, bt, num_tokens=wl.num_tokens,
+                                        block_size=wl.block_size, num_blocks=wl.num_blocks,
+                                        num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                                        head_dim=wl.head_dim, max_query_len=wl.max_query_len,
+                                        max_seq_len=wl.max_seq_len, split_tokens=64,
+                                        workspace=ws, out=prep)
+        else:
+            pkv.prepare_inputs(nst, nct, bt, num_tokens=wl.num_tokens, block_size=wl.block_size,
+                               num_blocks=wl.num_blocks, out=prep)
         pkv.kv_cache_write(key, value, kc, vc, prep["slot_mapping"], block_size=wl.block_size)
         pkv.paged_attention(q, kc, vc, prep["query_start_loc"], prep["seq_lens"], bt,
                             max_query_len=wl.max_query_len, max_seq_len=wl.max_seq_len,
-                            scale=wl.scale, out=out, split_tokens=64, workspace=ws)
+                            scale=wl.scale, out=out, split_tokens=64, workspace=ws,
+                            planned=fused)
 
     def eager_reference():
         kc.copy_(kc0)
