@@ -717,7 +717,7 @@ def roofline_of(work, t_ms):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path: the hot path is measured on one GPU's share at its real shape.",
               file=sys.stderr)
         sys.exit(2)

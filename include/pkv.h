@@ -94,7 +94,7 @@ extern "C" {
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes  */
-  PKV_ERR_UNSUPPORTED = 2, /* a valid argument this build has no kernel for    */
+  PKV_ERR_UNSUPPORTED = 2, /* a valid argument the library has no kernel for  */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
   PKV_ERR_LAUNCH = 4,      /* the HIP runtime rejected a kernel launch         */
   PKV_ERR_DEVICE_DATA = 5, /* checked build only: device data broke a
